@@ -1,0 +1,39 @@
+"""Writes tests/golden/tiny_block_exact.json from the float64 oracle.
+
+The pages print no worked numeric example for the block, so this fixture is
+not a page value: it is a regression record of the oracle itself (exact mode,
+tiny block, seed 0), written only by this script, which calls nothing but the
+oracle and the seeded input generators. Re-run it only when a change to the
+oracle's arithmetic is justified by a reading of the pages.
+"""
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
+
+import oracle as O  # noqa: E402
+from joint_attention_dit_amd.inputs import CONFIGS, make_inputs, to_numpy_f64  # noqa: E402
+
+ROWS = [0, 1, 31, 32, 33, 100, 200, 287]
+COLS = [0, 1, 2, 63, 64, 127, 128, 255]
+
+
+def compute():
+    cfg = CONFIGS["tiny"]
+    inp = make_inputs(cfg, seed=0)
+    w = {k: to_numpy_f64(inp[k]) for k in ("w_ada", "w_qkv", "w_o", "w_up", "w_down")}
+    r = O.block_forward(to_numpy_f64(inp["x"]), to_numpy_f64(inp["cond"]), w,
+                        inp["positions"].numpy(), heads=cfg.heads, mode="exact")
+    return {
+        "config": "tiny", "seed": 0, "mode": "exact", "rows": ROWS, "cols": COLS,
+        "out": [[r["out"][i, j] for j in COLS] for i in ROWS],
+        "x1": [[r["x1"][i, j] for j in COLS] for i in ROWS],
+        "mod_first8": list(r["mod"][:8]),
+    }
+
+
+if __name__ == "__main__":
+    with open(os.path.join(HERE, "tiny_block_exact.json"), "w") as f:
+        json.dump(compute(), f, indent=1)

@@ -1,0 +1,459 @@
+"""Pins for the float64 CPU oracle (no GPU).
+
+Each test ties an oracle function to something other than itself: a closed
+form, an invariant, a library routine (torch float64 ops, scipy) or brute
+force in pure Python. The pages print no worked numeric example for the
+block, so there are no page-printed values to compare against.
+"""
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle as O
+
+RNG = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------- bf16 rounding
+def _bf16_scalar(x: float) -> float:
+    """Pure-Python round-to-nearest-even onto the bf16 grid (8 significant bits).
+
+    Independent of numpy: math.frexp for the exponent, Python's round() (which
+    rounds halves to even) for the mantissa."""
+    if x == 0.0:
+        return 0.0
+    m, e = math.frexp(x)
+    e = max(e, -125)
+    q = round(x * 2.0 ** (8 - e))
+    return q * 2.0 ** (e - 8)
+
+
+def test_bf16_round_matches_torch_on_float32_values():
+    # torch's float32 -> bfloat16 conversion is round-to-nearest-even; for values
+    # that are exact float32 numbers, a direct float64 rounding must agree.
+    vals = np.concatenate([
+        RNG.standard_normal(20000) * s for s in (1e-30, 1e-6, 1e-2, 1.0, 3.0, 1e4, 1e30)
+    ]).astype(np.float32)
+    vals = np.concatenate([vals, np.float32([1e-40, -3e-39, 1.17e-38, 0.0, -0.0])])
+    ref = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(vals.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_round_ties_and_double_rounding():
+    u = 2.0 ** -8  # half an ulp of bf16 at 1.0
+    assert O.bf16_round(np.array([1 + u]))[0] == 1.0                  # tie -> even (down)
+    assert O.bf16_round(np.array([1 + 3 * u]))[0] == 1 + 4 * u        # tie -> even (up)
+    assert O.bf16_round(np.array([-(1 + u)]))[0] == -1.0
+    # a float64 value just above a tie must round up; rounding to float32 first
+    # would erase the excess and then round down to even
+    assert O.bf16_round(np.array([1 + u + 2.0 ** -40]))[0] == 1 + 2 * u
+    xs = RNG.standard_normal(5000) * 10.0 ** RNG.integers(-40, 30, 5000)
+    got = O.bf16_round(xs)
+    ref = np.array([_bf16_scalar(float(v)) for v in xs])
+    np.testing.assert_array_equal(got, ref)
+
+
+# ---------------------------------------------------------------- modulation
+def test_modulation_bruteforce():
+    D = 7
+    w = RNG.standard_normal((6 * D, D))
+    c = RNG.standard_normal(D)
+    ref = [sum(w[i][j] * c[j] for j in range(D)) for i in range(6 * D)]
+    np.testing.assert_allclose(O.modulation(w, c), ref, rtol=1e-13, atol=1e-13)
+    parts = O.split_modulation(O.modulation(w, c), D)
+    assert list(parts) == ["shift1", "scale1", "gate1", "shift2", "scale2", "gate2"]
+    np.testing.assert_array_equal(parts["gate1"], O.modulation(w, c)[2 * D:3 * D])
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rmsnorm_unit_rms_closed_form():
+    x = RNG.standard_normal((64, 300)) * RNG.uniform(0.01, 30, (64, 1))
+    eps = 1e-6
+    y = O.rms_normalize(x, eps)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), np.sqrt(ms / (ms + eps)),
+                               rtol=1e-13)
+    y0 = O.rms_normalize(x, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y0 * y0, axis=1)), 1.0, rtol=1e-13)
+
+
+def test_rmsnorm_matches_torch_library():
+    x = RNG.standard_normal((32, 256))
+    ref = F.rms_norm(torch.from_numpy(x), (256,), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rms_normalize(x, 1e-6), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_modulated_norm_special_cases():
+    x = RNG.standard_normal((5, 64))
+    zero = np.zeros(64)
+    # scale = -1, shift = 0 -> exactly zero
+    assert np.all(O.modulated_norm(x, zero, -np.ones(64), 1e-6, "exact") == 0.0)
+    # scale = 0, shift = s -> normalised x + s
+    s = RNG.standard_normal(64)
+    np.testing.assert_allclose(O.modulated_norm(x, s, zero, 1e-6, "exact"),
+                               O.rms_normalize(x, 1e-6) + s, rtol=0, atol=0)
+    # contract mode rounds to bf16 exactly once
+    y = O.modulated_norm(x, s, zero, 1e-6, "contract")
+    np.testing.assert_array_equal(y, O.bf16_round(O.rms_normalize(x, 1e-6) + s))
+
+
+# ---------------------------------------------------------------- RoPE
+def _rope_one(vec, row, col):
+    t = np.asarray(vec, dtype=np.float64).reshape(1, 1, 128)
+    return O.apply_rope(t, np.array([[row, col]]), 10000.0).reshape(128)
+
+
+def test_rope_identity_at_origin():
+    t = RNG.standard_normal((3, 4, 128))
+    np.testing.assert_array_equal(O.apply_rope(t, np.zeros((3, 2), np.int64), 10000.0), t)
+
+
+def test_rope_pair_structure_and_closed_angles():
+    # pair 0 of the row half turns by exactly `row` radians
+    e0 = np.zeros(128); e0[0] = 1.0
+    y = _rope_one(e0, 1, 0)
+    np.testing.assert_allclose(y[:2], [math.cos(1.0), math.sin(1.0)], atol=1e-15)
+    assert np.all(y[2:] == 0.0)
+    # pair 16 has theta = 10000**(-1/2) = 0.01: row 100 turns it by 1 rad
+    e32 = np.zeros(128); e32[32] = 1.0
+    y = _rope_one(e32, 100, 0)
+    np.testing.assert_allclose(y[32:34], [math.cos(1.0), math.sin(1.0)], atol=1e-13)
+    assert np.count_nonzero(y) == 2
+    # the column half: pair 0 of dims 64.. turns by `col` radians; the row does not touch it
+    e65 = np.zeros(128); e65[65] = 1.0
+    y = _rope_one(e65, 7, 2)
+    np.testing.assert_allclose(y[64:66], [-math.sin(2.0), math.cos(2.0)], atol=1e-15)
+    assert np.count_nonzero(y) == 2
+    # the column position leaves dims 0..63 alone, the row leaves 64..127 alone
+    v = RNG.standard_normal(128)
+    a, b = _rope_one(v, 5, 9), _rope_one(v, 5, 30)
+    np.testing.assert_array_equal(a[:64], b[:64])
+    c = _rope_one(v, 40, 9)
+    np.testing.assert_array_equal(a[64:], c[64:])
+
+
+def test_rope_preserves_norms():
+    t = RNG.standard_normal((50, 3, 128))
+    pos = RNG.integers(0, 320, (50, 2))
+    y = O.apply_rope(t, pos, 10000.0)
+    for a in range(2):
+        sl = slice(64 * a, 64 * a + 64)
+        np.testing.assert_allclose(np.linalg.norm(y[..., sl], axis=-1),
+                                   np.linalg.norm(t[..., sl], axis=-1), rtol=1e-13)
+    pairs_in = t[..., 0::2] ** 2 + t[..., 1::2] ** 2
+    pairs_out = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    np.testing.assert_allclose(pairs_out, pairs_in, rtol=1e-12)
+
+
+def test_rope_relative_positions():
+    # <R(a) q, R(b) k> depends only on a - b (translation of both positions)
+    q = RNG.standard_normal(128)
+    k = RNG.standard_normal(128)
+    d1 = _rope_one(q, 10, 3) @ _rope_one(k, 4, 20)
+    d2 = _rope_one(q, 106, 53) @ _rope_one(k, 100, 70)
+    np.testing.assert_allclose(d1, d2, rtol=1e-11)
+    # and the complex-number view: pair (u, w) times exp(i * angle)
+    theta = 10000.0 ** (-np.arange(32) / 32.0)
+    z = q[0:64:2] + 1j * q[1:64:2]
+    zr = z * np.exp(1j * 10 * theta)
+    y = _rope_one(q, 10, 0)
+    np.testing.assert_allclose(y[0:64:2], zr.real, atol=1e-13)
+    np.testing.assert_allclose(y[1:64:2], zr.imag, atol=1e-13)
+
+
+# ---------------------------------------------------------------- attention
+def _attention_bruteforce(q, k, v):
+    """Triple-loop softmax attention in pure Python floats."""
+    Tq, H, dh = q.shape
+    Tk = k.shape[0]
+    out = np.zeros((Tq, H, dh))
+    for h in range(H):
+        for i in range(Tq):
+            s = [sum(q[i, h, d] * k[j, h, d] for d in range(dh)) / math.sqrt(dh) for j in range(Tk)]
+            m = max(s)
+            p = [math.exp(x - m) for x in s]
+            z = sum(p)
+            for d in range(dh):
+                out[i, h, d] = sum(p[j] * v[j, h, d] for j in range(Tk)) / z
+    return out
+
+
+def test_attention_bruteforce_tiny():
+    q = RNG.standard_normal((5, 2, 4)) * 2
+    k = RNG.standard_normal((7, 2, 4)) * 2
+    v = RNG.standard_normal((7, 2, 4))
+    np.testing.assert_allclose(O.attention(q, k, v, "exact"), _attention_bruteforce(q, k, v),
+                               rtol=1e-12, atol=1e-13)
+
+
+def _contract_bruteforce(q, k, v):
+    """The rounded-weights form in pure Python: bf16 via _bf16_scalar."""
+    Tq, H, dh = q.shape
+    Tk = k.shape[0]
+    c = math.log2(math.e) / math.sqrt(dh)
+    out = np.zeros((Tq, H, dh))
+    for h in range(H):
+        for i in range(Tq):
+            s = [sum(q[i, h, d] * k[j, h, d] for d in range(dh)) * c for j in range(Tk)]
+            m = math.ceil(max(s))
+            p = [_bf16_scalar(2.0 ** (x - m)) for x in s]
+            z = sum(p)
+            for d in range(dh):
+                out[i, h, d] = _bf16_scalar(sum(p[j] * v[j, h, d] for j in range(Tk)) / z)
+    return out
+
+
+def test_attention_contract_bruteforce_tiny():
+    q = O.bf16_round(RNG.standard_normal((4, 2, 8)) * 3)
+    k = O.bf16_round(RNG.standard_normal((9, 2, 8)) * 3)
+    v = O.bf16_round(RNG.standard_normal((9, 2, 8)))
+    got = O.attention(q, k, v, "contract")
+    ref = _contract_bruteforce(q, k, v)
+    # the sums may differ in the last float64 bit, which can flip a bf16 rounding
+    # of o only at an exact tie; require near-equality and mostly exact equality
+    np.testing.assert_allclose(got, ref, rtol=2 ** -8, atol=0)
+    assert np.mean(got == ref) > 0.97
+
+
+def test_attention_matches_torch_sdpa():
+    q = RNG.standard_normal((33, 3, 128))
+    k = RNG.standard_normal((40, 3, 128))
+    v = RNG.standard_normal((40, 3, 128))
+    tq, tk, tv = (torch.from_numpy(a).permute(1, 0, 2) for a in (q, k, v))
+    ref = F.scaled_dot_product_attention(tq, tk, tv).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(O.attention(q, k, v, "exact"), ref, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["exact", "contract"])
+def test_attention_special_cases(mode):
+    v = O.bf16_round(RNG.standard_normal((9, 2, 128)))
+    k = O.bf16_round(RNG.standard_normal((9, 2, 128)))
+    # a single key returns its value
+    q1 = O.bf16_round(RNG.standard_normal((3, 2, 128)) * 5)
+    np.testing.assert_array_equal(O.attention(q1, k[:1], v[:1], mode),
+                                  np.broadcast_to(v[:1], (3, 2, 128)))
+    # zero queries: uniform weights -> mean of the values
+    q0 = np.zeros((2, 2, 128))
+    ref = np.broadcast_to(v.mean(axis=0, keepdims=True), (2, 2, 128))
+    got = O.attention(q0, k, v, mode)
+    tol = 2 ** -8 * np.abs(ref).max() if mode == "contract" else 1e-14
+    np.testing.assert_allclose(got, ref, atol=tol, rtol=0)
+    # one dominant key: output -> its value
+    qd = k[4:5] * 50.0
+    np.testing.assert_allclose(O.attention(qd, k, v, mode)[0], v[4], atol=1e-12)
+    # permuting the keys (with their values) changes nothing
+    qq = RNG.standard_normal((4, 2, 128))
+    perm = RNG.permutation(9)
+    a = O.attention(qq, k, v, mode)
+    b = O.attention(qq, k[perm], v[perm], mode)
+    if mode == "exact":
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+    else:
+        np.testing.assert_allclose(a, b, rtol=2 ** -7, atol=1e-12)
+
+
+def test_attention_contract_close_to_exact():
+    q = O.bf16_round(RNG.standard_normal((64, 2, 128)))
+    k = O.bf16_round(RNG.standard_normal((200, 2, 128)))
+    v = O.bf16_round(RNG.standard_normal((200, 2, 128)))
+    a = O.attention(q, k, v, "exact")
+    b = O.attention(q, k, v, "contract")
+    # rounded weights carry relative error <= 2**-9 each; o is rounded once more
+    bound = 2 ** -9 * 2 * np.abs(v).max() + 2 ** -9 * np.abs(a)
+    assert np.all(np.abs(a - b) <= bound + 1e-12)
+
+
+# ---------------------------------------------------------------- GELU
+def test_gelu_matches_torch_and_identities():
+    z = np.linspace(-12, 12, 10001)
+    ref = F.gelu(torch.from_numpy(z), approximate="tanh").numpy()
+    np.testing.assert_allclose(O.gelu_tanh(z), ref, rtol=1e-14, atol=1e-15)
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    # g(z) - g(-z) = z for the tanh form (tanh is odd)
+    np.testing.assert_allclose(O.gelu_tanh(z) - O.gelu_tanh(-z), z, atol=1e-13)
+    # it approximates the erf form to within 5e-4 everywhere
+    from scipy.special import erf
+    exact = 0.5 * z * (1 + erf(z / math.sqrt(2)))
+    assert np.max(np.abs(O.gelu_tanh(z) - exact)) < 5e-4
+
+
+# ---------------------------------------------------------------- whole block
+def _micro_inputs(T=6, D=8, H=2, Fd=16, seed=7):
+    r = np.random.default_rng(seed)
+    A = H * 128
+    w = dict(w_ada=O.bf16_round(r.standard_normal((6 * D, D)) * 0.3),
+             w_qkv=O.bf16_round(r.standard_normal((3 * A, D)) * 0.3),
+             w_o=O.bf16_round(r.standard_normal((D, A)) * 0.05),
+             w_up=O.bf16_round(r.standard_normal((Fd, D)) * 0.3),
+             w_down=O.bf16_round(r.standard_normal((D, Fd)) * 0.3))
+    x = r.standard_normal((T, D))
+    cond = r.standard_normal(D)
+    pos = np.array([[0, 0]] * 2 + [[r_, c_] for r_ in range(2) for c_ in range(2)])[:T]
+    return x, cond, w, pos, H
+
+
+def _scalar_block(x, cond, w, pos, H, eps=1e-6, base=10000.0):
+    """The whole block in plain Python loops (exact mode)."""
+    T, D = x.shape
+    A = H * 128
+    Fd = w["w_up"].shape[0]
+    mod = [sum(w["w_ada"][i][j] * cond[j] for j in range(D)) for i in range(6 * D)]
+    sh1, sc1, g1, sh2, sc2, g2 = (mod[i * D:(i + 1) * D] for i in range(6))
+
+    def norm(row, sh, sc):
+        ms = sum(v * v for v in row) / len(row)
+        r = 1.0 / math.sqrt(ms + eps)
+        return [row[j] * r * (1 + sc[j]) + sh[j] for j in range(len(row))]
+
+    def rope(vec, p):
+        out = list(vec)
+        for h in range(H):
+            for a in range(2):
+                for i in range(32):
+                    d = h * 128 + 64 * a + 2 * i
+                    ang = p[a] * base ** (-2.0 * i / 64)
+                    out[d] = vec[d] * math.cos(ang) - vec[d + 1] * math.sin(ang)
+                    out[d + 1] = vec[d] * math.sin(ang) + vec[d + 1] * math.cos(ang)
+        return out
+
+    h1 = [norm(list(x[t]), sh1, sc1) for t in range(T)]
+    proj = [[sum(h1[t][j] * w["w_qkv"][n][j] for j in range(D)) for n in range(3 * A)]
+            for t in range(T)]
+    q = [rope(proj[t][:A], pos[t]) for t in range(T)]
+    k = [rope(proj[t][A:2 * A], pos[t]) for t in range(T)]
+    v = [proj[t][2 * A:] for t in range(T)]
+    o = [[0.0] * A for _ in range(T)]
+    for h in range(H):
+        for i in range(T):
+            s = [sum(q[i][h * 128 + d] * k[j][h * 128 + d] for d in range(128)) / math.sqrt(128)
+                 for j in range(T)]
+            m = max(s)
+            p = [math.exp(z - m) for z in s]
+            zs = sum(p)
+            for d in range(128):
+                o[i][h * 128 + d] = sum(p[j] * v[j][h * 128 + d] for j in range(T)) / zs
+    out = []
+    for t in range(T):
+        x1 = [x[t][n] + g1[n] * sum(o[t][a] * w["w_o"][n][a] for a in range(A)) for n in range(D)]
+        h2 = norm(x1, sh2, sc2)
+        u = []
+        for f in range(Fd):
+            zz = sum(h2[j] * w["w_up"][f][j] for j in range(D))
+            u.append(0.5 * zz * (1 + math.tanh(math.sqrt(2 / math.pi) * (zz + 0.044715 * zz ** 3))))
+        out.append([x1[n] + g2[n] * sum(u[f] * w["w_down"][n][f] for f in range(Fd)) for n in range(D)])
+    return np.array(out)
+
+
+def test_block_matches_scalar_loops():
+    x, cond, w, pos, H = _micro_inputs()
+    ref = _scalar_block(x, cond, w, pos, H)
+    got = O.block_forward(x, cond, w, pos, heads=H, mode="exact")["out"]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def _torch_block_exact(x, cond, w, pos, H, eps=1e-6, base=10000.0):
+    """Exact-mode block from torch float64 library ops; RoPE as complex rotation."""
+    t = {k: torch.from_numpy(v) for k, v in w.items()}
+    x = torch.from_numpy(x)
+    T, D = x.shape
+    A = H * 128
+    mod = F.linear(torch.from_numpy(cond), t["w_ada"])
+    sh1, sc1, g1, sh2, sc2, g2 = mod.split(D)
+    h1 = F.rms_norm(x, (D,), eps=eps) * (1 + sc1) + sh1
+    q, k, v = F.linear(h1, t["w_qkv"]).split(A, dim=1)
+    theta = base ** (-torch.arange(32, dtype=torch.float64) / 32.0)
+    p = torch.from_numpy(pos).to(torch.float64)
+
+    def rope(z):
+        z = z.reshape(T, H, 2, 32, 2)
+        zc = torch.view_as_complex(z.contiguous())                        # [T, H, 2, 32]
+        rot = torch.polar(torch.ones(T, 2, 32, dtype=torch.float64),
+                          p[:, :, None] * theta[None, None, :])          # [T, 2, 32]
+        return torch.view_as_real(zc * rot[:, None]).reshape(T, H, 128)
+
+    q, k = rope(q), rope(k)
+    v = v.reshape(T, H, 128)
+    o = F.scaled_dot_product_attention(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1))
+    o = o.transpose(0, 1).reshape(T, A)
+    x1 = x + g1 * F.linear(o, t["w_o"])
+    h2 = F.rms_norm(x1, (D,), eps=eps) * (1 + sc2) + sh2
+    u = F.gelu(F.linear(h2, t["w_up"]), approximate="tanh")
+    return (x1 + g2 * F.linear(u, t["w_down"])).numpy()
+
+
+def _tiny_f64():
+    from joint_attention_dit_amd.inputs import CONFIGS, make_inputs, to_numpy_f64
+    cfg = CONFIGS["tiny"]
+    inp = make_inputs(cfg, seed=0)
+    w = {k: to_numpy_f64(inp[k]) for k in ("w_ada", "w_qkv", "w_o", "w_up", "w_down")}
+    return cfg, to_numpy_f64(inp["x"]), to_numpy_f64(inp["cond"]), w, inp["positions"].numpy()
+
+
+def test_block_matches_torch_library_composite_tiny():
+    cfg, x, cond, w, pos = _tiny_f64()
+    ref = _torch_block_exact(x, cond, w, pos, cfg.heads)
+    got = O.block_forward(x, cond, w, pos, heads=cfg.heads, mode="exact")["out"]
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_block_contract_close_to_exact_tiny():
+    cfg, x, cond, w, pos = _tiny_f64()
+    a = O.block_forward(x, cond, w, pos, heads=cfg.heads, mode="exact")["out"]
+    b = O.block_forward(x, cond, w, pos, heads=cfg.heads, mode="contract")["out"]
+    rel = np.linalg.norm(a - b) / np.linalg.norm(a)
+    assert 0 < rel < 5e-3
+
+
+@pytest.mark.parametrize("mode", ["exact", "contract"])
+def test_block_zero_gates_return_input(mode):
+    cfg, x, cond, w, pos = _tiny_f64()
+    D = cfg.hidden
+    w = dict(w)
+    w["w_ada"] = w["w_ada"].copy()
+    w["w_ada"][2 * D:3 * D] = 0.0        # gate1
+    w["w_ada"][5 * D:6 * D] = 0.0        # gate2
+    r = O.block_forward(x, cond, w, pos, heads=cfg.heads, mode=mode)
+    np.testing.assert_array_equal(r["out"], x)
+    # with only gate1 zero, x1 == x
+    w2 = dict(w)
+    w2["w_ada"] = _tiny_f64()[3]["w_ada"].copy()
+    w2["w_ada"][2 * D:3 * D] = 0.0
+    np.testing.assert_array_equal(O.block_forward(x, cond, w2, pos, heads=cfg.heads, mode=mode)["x1"], x)
+
+
+def test_block_scale_minus_one_kills_attention_branch():
+    cfg, x, cond, w, pos = _tiny_f64()
+    D = cfg.hidden
+    w = dict(w)
+    w["w_ada"] = w["w_ada"].copy()
+    cond1 = np.zeros(D); cond1[0] = 1.0
+    w["w_ada"][:, :] = 0.0
+    w["w_ada"][D:2 * D, 0] = -1.0        # scale1 = -1, shift1 = 0
+    w["w_ada"][2 * D:3 * D, 0] = 0.5     # gate1 = 0.5
+    r = O.block_forward(x, cond1, w, pos, heads=cfg.heads, mode="contract")
+    assert np.all(r["h1"] == 0.0) and np.all(r["o"] == 0.0)
+    np.testing.assert_array_equal(r["x1"], x)
+
+
+def test_block_permutation_and_translation_equivariance():
+    x, cond, w, pos, H = _micro_inputs(T=6, seed=3)
+    base = O.block_forward(x, cond, w, pos, heads=H, mode="exact")["out"]
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    got = O.block_forward(x[perm], cond, w, pos[perm], heads=H, mode="exact")["out"]
+    np.testing.assert_allclose(got, base[perm], rtol=1e-12, atol=1e-12)
+    shifted = O.block_forward(x, cond, w, pos + np.array([17, 5]), heads=H, mode="exact")["out"]
+    np.testing.assert_allclose(shifted, base, rtol=1e-10, atol=1e-10)
+
+
+def test_block_row_sampling_matches_full():
+    cfg, x, cond, w, pos = _tiny_f64()
+    full = O.block_forward(x, cond, w, pos, heads=cfg.heads, mode="contract")
+    rows = np.array([0, 5, 31, 32, 100, 287])
+    part = O.block_forward(x, cond, w, pos, heads=cfg.heads, mode="contract", rows=rows)
+    for key in ("o", "x1", "h2", "u", "out"):
+        np.testing.assert_allclose(part[key], full[key][rows], rtol=1e-9, atol=1e-9)
