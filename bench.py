@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of one MiniMax-H3-Image DiT block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4096]
+
+One step = one h3dit_block_forward over the whole joint sequence (all nine
+steps of the block: modulation, RoPE table, RMSNorm1, QKV+RoPE GEMM,
+attention, output projection, RMSNorm2, MLP up+GELU, MLP down), inputs and
+weights resident in HBM before the timed region starts. Prints ONE JSON line.
+
+Per-kernel times come from HIP events that the library records between its
+kernel launches on the same stream (h3dit_block_forward_timed), averaged over
+the timed steps; the roofline object reports the slowest kernel.
+
+The cpu_baseline leg times the float64 CPU oracle on a bounded sample of the
+same workload (a few sampled query rows; keys and values still cover every
+token) and extrapolates linearly in the number of rows to a whole block.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "DiT block tokens/s + TFLOP/s (% bf16 MFMA peak), 4096/16384 image tokens"
+
+STAGES = ["modulation", "rope_table", "rmsnorm1", "qkv_rope_gemm", "attention", "out_proj_gemm",
+          "rmsnorm2", "mlp_up_gelu_gemm", "mlp_down_gemm"]
+
+
+def stage_work(cfg):
+    """Algorithmic FLOPs / HBM bytes of each kernel of one block (per launch)."""
+    T, D, A, F = cfg.n_tokens, cfg.hidden, cfg.attn_width, cfg.ffn
+    xb = 4 if cfg.x_dtype == "fp32" else 2
+    flops = {
+        "modulation": 2.0 * 6 * D * D,
+        "qkv_rope_gemm": 2.0 * T * D * 3 * A,
+        "attention": 4.0 * T * T * A,
+        "out_proj_gemm": 2.0 * T * A * D,
+        "mlp_up_gelu_gemm": 2.0 * T * D * F,
+        "mlp_down_gemm": 2.0 * T * F * D,
+    }
+    nbytes = {
+        "modulation": 2.0 * 6 * D * D + 4 * D + 8 * 6 * D,
+        "rope_table": 8.0 * T + 4.0 * T * 128,
+        "rmsnorm1": (xb + 2.0) * T * D,
+        "rmsnorm2": (4.0 + 2.0) * T * D,
+        "qkv_rope_gemm": 2.0 * T * D + 2.0 * 3 * A * D + 2.0 * T * 3 * A + 4.0 * T * 128,
+        "attention": 2.0 * T * 3 * A + 2.0 * T * A,
+        "out_proj_gemm": 2.0 * T * A + 2.0 * D * A + (xb + 4.0) * T * D,
+        "mlp_up_gelu_gemm": 2.0 * T * D + 2.0 * F * D + 2.0 * T * F,
+        "mlp_down_gemm": 2.0 * T * F + 2.0 * D * F + 8.0 * T * D,
+    }
+    return flops, nbytes
+
+
+def block_flops(cfg) -> float:
+    T, D, A, F = cfg.n_tokens, cfg.hidden, cfg.attn_width, cfg.ffn
+    return 2.0 * T * (3 * A * D + A * D + 2 * D * F) + 4.0 * T * T * A + 2.0 * 6 * D * D
+
+
+def measure(cfg, steps: int, warmup: int):
+    import torch
+    from joint_attention_dit_amd import binding as B
+    from joint_attention_dit_amd.inputs import make_inputs
+
+    inp = make_inputs(cfg, seed=0)
+    blk = B.Block(cfg, inp, device="cuda:0")
+    del inp
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        blk.forward(stream)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+          for _ in range(steps)]
+    for row in ev:          # torch creates the underlying hipEvent_t on first record
+        for e in row:
+            e.record(stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    assert all(e.cuda_event for row in ev for e in row)
+    start.record(stream)
+    for k in range(steps):
+        blk.forward_timed([e.cuda_event for e in ev[k]], stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    stage_ms = {s: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)) / steps
+                for i, s in enumerate(STAGES)}
+    out_ok = bool(torch.isfinite(blk.out).all().item())
+    del blk
+    torch.cuda.empty_cache()
+    return ms, stage_ms, out_ok
+
+
+def summarize(cfg, ms, stage_ms):
+    flops, nbytes = stage_work(cfg)
+    total = block_flops(cfg)
+    tflops = total / (ms * 1e-3) / 1e12
+    kernels = {}
+    for s in STAGES:
+        t = stage_ms[s] * 1e-3
+        k = {"ms": round(stage_ms[s], 4)}
+        if s in flops and s != "modulation":
+            k["tflops"] = round(flops[s] / t / 1e12, 1)
+            k["pct_mfma_peak"] = round(100 * flops[s] / t / 1e12 / PEAK_BF16_TFLOPS, 1)
+        else:
+            k["gbs"] = round(nbytes[s] / t / 1e9, 1)
+            k["pct_hbm_peak"] = round(100 * nbytes[s] / t / 1e9 / PEAK_HBM_GBS, 1)
+        kernels[s] = k
+    dom = max(STAGES, key=lambda s: stage_ms[s])
+    t = stage_ms[dom] * 1e-3
+    if dom in flops and dom != "modulation":
+        ach = flops[dom] / t / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_per_launch": flops[dom]}
+    else:
+        ach = nbytes[dom] / t / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_per_launch": nbytes[dom]}
+    return tflops, kernels, roof
+
+
+def cpu_baseline(cfg, rows_small: int, rows_large: int):
+    """Time the float64 oracle at two row counts; extrapolate linearly to all T rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from joint_attention_dit_amd.inputs import make_inputs, sample_rows, to_numpy_f64
+
+    inp = make_inputs(cfg, seed=0)
+    w = {k: to_numpy_f64(inp[k]) for k in ("w_ada", "w_qkv", "w_o", "w_up", "w_down")}
+    x, cond, pos = to_numpy_f64(inp["x"]), to_numpy_f64(inp["cond"]), inp["positions"].numpy()
+    del inp
+    times = {}
+    for r in (rows_small, rows_large):
+        rows = sample_rows(cfg.n_tokens, r, seed=1)
+        t0 = time.perf_counter()
+        O.block_forward(x, cond, w, pos, heads=cfg.heads, eps=cfg.eps, rope_base=cfg.rope_base,
+                        mode="contract", rows=rows)
+        times[r] = time.perf_counter() - t0
+    per_row = max((times[rows_large] - times[rows_small]) / (rows_large - rows_small), 0.0)
+    fixed = max(times[rows_small] - per_row * rows_small, 0.0)
+    t_block = fixed + per_row * cfg.n_tokens
+    threads = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = max(threads) if threads else len(os.sched_getaffinity(0))
+    return {
+        "value": round(cfg.n_tokens / t_block, 2), "unit": "block-tokens/s", "cores": cores,
+        "kind": "oracle",
+        "sample": (f"float64 oracle (contract mode) on the same {cfg.n_tokens}-token block with "
+                   f"{rows_small} and {rows_large} sampled query rows (keys/values over all tokens): "
+                   f"{times[rows_small]:.2f} s and {times[rows_large]:.2f} s; linear extrapolation "
+                   f"to all rows gives {t_block:.1f} s per block"),
+        "seconds_measured": round(times[rows_small] + times[rows_large], 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="4096", choices=["2048", "4096", "edit", "nonsquare", "tiny"])
+    ap.add_argument("--extra", default="2048", help="second workload reported under 'extra' ('' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", default="8,40", help="row counts of the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the block runs on a single MI355X and this build "
+              "has no multi-GPU path (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from joint_attention_dit_amd.inputs import CONFIGS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = CONFIGS[args.workload]
+    ms, stage_ms, ok = measure(cfg, args.steps, args.warmup)
+    tflops, kernels, roof = summarize(cfg, ms, stage_ms)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(cfg.n_tokens / (ms * 1e-3), 1),
+        "unit": "block-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights)",
+        "config": {"workload": cfg.description, "n_tokens": cfg.n_tokens,
+                   "image_tokens": cfg.image_tokens, "text_tokens": cfg.text_tokens,
+                   "hidden": cfg.hidden, "heads": cfg.heads, "head_dim": cfg.head_dim,
+                   "ffn": cfg.ffn},
+        "tflops": round(tflops, 1),
+        "pct_bf16_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "image_tokens_per_s": round(cfg.image_tokens / (ms * 1e-3), 1),
+        "output_finite": ok,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if args.extra and args.extra != args.workload:
+        ecfg = CONFIGS[args.extra]
+        ems, est, eok = measure(ecfg, max(args.steps // 2, 1), max(args.warmup // 2, 1))
+        etf, ekern, eroof = summarize(ecfg, ems, est)
+        rec["extra"] = {"workload": ecfg.description, "n_tokens": ecfg.n_tokens,
+                        "ms_per_step": round(ems, 4), "value": round(ecfg.n_tokens / (ems * 1e-3), 1),
+                        "unit": "block-tokens/s", "tflops": round(etf, 1),
+                        "pct_bf16_mfma_peak": round(100 * etf / PEAK_BF16_TFLOPS, 2),
+                        "kernels": ekern}
+    if not args.no_cpu_baseline:
+        r1, r2 = (int(v) for v in args.cpu_rows.split(","))
+        rec["cpu_baseline"] = cpu_baseline(cfg, r1, r2)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * h3dit.h - C ABI of the MI355X (gfx950) library for one MiniMax-H3-Image DiT
+ * block forward pass over the packed joint sequence of text and image tokens.
+ *
+ * What one block computes (apxml.com spec page, "Architecture Diagram", read
+ * together with the Hugging Face model card, "Model Architecture"):
+ *
+ *   mod  = W_ada . cond                      -> shift1 scale1 gate1 shift2 scale2 gate2
+ *   h1   = rmsnorm(x) * (1 + scale1) + shift1
+ *   q,k,v = h1 . W_qkv^T ; q,k rotated by 2D axial RoPE
+ *   o    = softmax(q k^T / sqrt(128)) v      (per head, all tokens, no mask)
+ *   x1   = x + gate1 * (o . W_o^T)
+ *   h2   = rmsnorm(x1) * (1 + scale2) + shift2
+ *   out  = x1 + gate2 * (gelu_tanh(h2 . W_up^T) . W_down^T)
+ *
+ * Conventions fixed here where the pages are silent: no biases; RMSNorm has
+ * no learned weight; RoPE rotates adjacent pairs (2i, 2i+1), dims 0..63 by
+ * the row position and 64..127 by the column position, with frequency
+ * rope_base^(-2i/64); text tokens use position (0, 0); GELU is the tanh form.
+ *
+ * Precision: weights and matrix-core operands are bf16 (round to nearest
+ * even); products accumulate in fp32; the modulation vector and both
+ * normalisations are computed in fp64; x1 and the output are fp32. The
+ * attention weights are bf16(2^(s - ceil(running max of s))) with
+ * s = q.k * log2(e)/sqrt(128), normalised by their own sum.
+ *
+ * Memory: every pointer argument is a DEVICE pointer unless marked (host);
+ * matrices are row-major and dense; the caller owns all memory, including the
+ * workspace; the library allocates nothing and keeps no device state.
+ * Every device pointer must be 16-byte aligned.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ * stream) and the call returns at once. Outputs are valid once the stream
+ * has been synchronised. Device faults surface at the next synchronisation.
+ *
+ * Errors: every argument check runs on the host before any HIP call; a
+ * failing check returns a negative h3dit_status and leaves all memory
+ * untouched. h3dit_last_error() then describes the failure (thread-local).
+ * A failed kernel launch returns H3DIT_EHIP. There is no CPU fallback.
+ *
+ * Threads: calls are reentrant for distinct workspaces / outputs.
+ */
+#ifndef H3DIT_H
+#define H3DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    H3DIT_OK = 0,
+    H3DIT_EINVAL = -1,       /* null pointer, bad size, bad enum value          */
+    H3DIT_EUNSUPPORTED = -2, /* valid but unsupported shape (e.g. head_dim != 128) */
+    H3DIT_EWORKSPACE = -3,   /* workspace smaller than h3dit_workspace_size()   */
+    H3DIT_EALIGN = -4,       /* a device pointer is not 16-byte aligned         */
+    H3DIT_EHIP = -5          /* a HIP launch reported an error                  */
+} h3dit_status;
+
+typedef enum { H3DIT_BF16 = 0, H3DIT_F32 = 1 } h3dit_dtype;
+
+/* Block shape (host struct). D = hidden, A = heads * head_dim, F = ffn, T = n_tokens.
+ * Requirements: head_dim == 128; hidden, ffn multiples of 64; heads >= 1;
+ * 1 <= n_tokens <= 1048576; hidden <= 65536; eps >= 0; rope_base > 0. */
+typedef struct {
+    int32_t hidden;     /* D: model width (5376 for the full-width block)            */
+    int32_t heads;      /* H: attention heads (56)                                    */
+    int32_t head_dim;   /* must be 128                                                */
+    int32_t ffn;        /* F: MLP inner width (14336)                                 */
+    int32_t n_tokens;   /* T: joint sequence length (text + image tokens)             */
+    int32_t x_dtype;    /* h3dit_dtype of the block input x                           */
+    float eps;          /* RMSNorm epsilon (1e-6)                                     */
+    float rope_base;    /* RoPE base (10000)                                          */
+} h3dit_config;
+
+/* Block weights (host struct of device pointers), all bf16 row-major [out, in]. */
+typedef struct {
+    const void *w_ada;  /* [6D, D]  rows: shift1 | scale1 | gate1 | shift2 | scale2 | gate2 */
+    const void *w_qkv;  /* [3A, D]  rows: q | k | v, each head-major (head h = rows h*128..) */
+    const void *w_o;    /* [D, A]                                                         */
+    const void *w_up;   /* [F, D]                                                         */
+    const void *w_down; /* [D, F]                                                         */
+} h3dit_weights;
+
+/* Bytes of device workspace h3dit_block_forward needs for this shape.
+ * Host-only; no HIP call. Returns H3DIT_OK and writes *bytes. */
+int h3dit_workspace_size(const h3dit_config *cfg, size_t *bytes);
+
+/* One DiT block forward (all nine steps of the block).
+ *   x          [T, D], dtype cfg->x_dtype (bf16 or fp32)
+ *   cond       [D] fp32 conditioning vector (the timestep embedding)
+ *   w          weights (see h3dit_weights)
+ *   positions  [T, 2] int32 RoPE positions (row, col); any int32 values
+ *   out        [T, D] fp32; must not overlap x or the workspace
+ *   workspace  >= h3dit_workspace_size() bytes; contents are scratch
+ */
+int h3dit_block_forward(const h3dit_config *cfg, const void *x, const float *cond,
+                        const h3dit_weights *w, const int32_t *positions, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Same as h3dit_block_forward, and records caller-created hipEvent_t handles
+ * between the stages: events[i] is recorded on `stream` before stage i and
+ * events[9] after the last, for stages (0) modulation, (1) RoPE table,
+ * (2) RMSNorm1, (3) QKV+RoPE GEMM, (4) attention, (5) output projection,
+ * (6) RMSNorm2, (7) MLP up + GELU, (8) MLP down. n_events must be 10. */
+int h3dit_block_forward_timed(const h3dit_config *cfg, const void *x, const float *cond,
+                              const h3dit_weights *w, const int32_t *positions, float *out,
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              void *const *events, int n_events);
+
+/* ---------------------------------------------------------------------------
+ * Stage entry points: the same kernels that h3dit_block_forward runs, one
+ * step at a time, for per-step parity checks and profiling. Shapes come from
+ * cfg; layouts are the workspace layouts named below.
+ * ------------------------------------------------------------------------- */
+
+/* Step 1, AdaLN modulation (spec page diagram, "AdaLN Modulation"):
+ * mod[6D] fp64 = W_ada[6D, D] (bf16) . cond[D] (fp32), fp64 accumulation. */
+int h3dit_modulation(const h3dit_config *cfg, const void *w_ada, const float *cond,
+                     double *mod, void *stream);
+
+/* Steps 2 and 7, RMSNorm + modulation (spec page, "RMS Normalization"):
+ * h[T, D] bf16 = bf16( x / sqrt(mean(x^2) + eps) * (1 + scale) + shift ),
+ * computed in fp64; x is [T, D] of dtype x_dtype; shift, scale are fp64 [D]. */
+int h3dit_rmsnorm_modulate(const h3dit_config *cfg, const void *x, int32_t x_dtype,
+                           const double *shift, const double *scale, void *h, void *stream);
+
+/* RoPE table for step 4 (model card: multimodal RoPE; 2D axial reading):
+ * table[T, 64, 2] fp32: (cos, sin) of positions[t][j / 32] * rope_base^(-(j % 32)/32),
+ * evaluated in fp64. */
+int h3dit_rope_table(const h3dit_config *cfg, const int32_t *positions, float *table,
+                     void *stream);
+
+/* Steps 3 + 4, QKV projection with RoPE in the epilogue:
+ *   h [T, D] bf16, w_qkv [3A, D] bf16, table from h3dit_rope_table.
+ *   qk [T, 2A] bf16: columns 0..A-1 = bf16(rope(bf16(q))), A..2A-1 = same for k.
+ *   vt [H, 128, Tp] bf16 with Tp = h3dit_padded_tokens(T): v transposed per head,
+ *      columns T..Tp-1 written as zero. */
+int h3dit_qkv_rope(const h3dit_config *cfg, const void *h, const void *w_qkv, const float *table,
+                   void *qk, void *vt, void *stream);
+
+/* Step 5, joint bidirectional attention over all T tokens (no mask):
+ *   qk, vt as written by h3dit_qkv_rope; o [T, A] bf16 (head h = columns h*128..). */
+int h3dit_attention(const h3dit_config *cfg, const void *qk, const void *vt, void *o,
+                    void *stream);
+
+/* Step 6, output projection + gated residual:
+ *   x1[T, D] fp32 = resid + gate * (o[T, A] . w_o[D, A]^T); resid is [T, D] of
+ *   dtype resid_dtype; gate fp64 [D]. */
+int h3dit_out_proj_residual(const h3dit_config *cfg, const void *o, const void *w_o,
+                            const void *resid, int32_t resid_dtype, const double *gate,
+                            float *x1, void *stream);
+
+/* Step 8, MLP up-projection + tanh-GELU:
+ *   u[T, F] bf16 = bf16(gelu_tanh(h2[T, D] . w_up[F, D]^T)). */
+int h3dit_mlp_up_gelu(const h3dit_config *cfg, const void *h2, const void *w_up, void *u,
+                      void *stream);
+
+/* Step 9, MLP down-projection + gated residual:
+ *   out[T, D] fp32 = x1 + gate * (u[T, F] . w_down[D, F]^T); x1 fp32, gate fp64 [D]. */
+int h3dit_mlp_down_residual(const h3dit_config *cfg, const void *u, const void *w_down,
+                            const float *x1, const double *gate, float *out, void *stream);
+
+/* Padded token count used by the vt layout (T rounded up to a multiple of 64). */
+int64_t h3dit_padded_tokens(int64_t n_tokens);
+
+/* Human-readable name of a status code (static string). */
+const char *h3dit_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *h3dit_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3DIT_H */

@@ -1,0 +1,240 @@
+"""Thin ctypes binding of libh3dit.so (include/h3dit.h), same names as the C ABI.
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, and a negative status becomes an exception.
+Every step of the block runs in the library's HIP kernels; there is no
+fallback. Importing this module on a machine without the built library
+raises at once.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libh3dit.so")
+
+H3DIT_OK, H3DIT_EINVAL, H3DIT_EUNSUPPORTED, H3DIT_EWORKSPACE, H3DIT_EALIGN, H3DIT_EHIP = \
+    0, -1, -2, -3, -4, -5
+H3DIT_BF16, H3DIT_F32 = 0, 1
+
+EXPORTED = (
+    "h3dit_workspace_size", "h3dit_block_forward", "h3dit_block_forward_timed",
+    "h3dit_modulation", "h3dit_rmsnorm_modulate", "h3dit_rope_table", "h3dit_qkv_rope",
+    "h3dit_attention", "h3dit_out_proj_residual", "h3dit_mlp_up_gelu",
+    "h3dit_mlp_down_residual", "h3dit_padded_tokens", "h3dit_status_string",
+    "h3dit_last_error",
+)
+
+
+class H3ditError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name} failed: {detail or 'no detail'} (status {status})")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("ffn", ctypes.c_int32),
+                ("n_tokens", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("w_ada", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p),
+                ("w_o", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libh3dit.so from the package directory (fails loudly if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m joint_attention_dit_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(Config)
+    sigs = {
+        "h3dit_workspace_size": [cfgp, ctypes.POINTER(sz)],
+        "h3dit_block_forward": [cfgp, vp, vp, ctypes.POINTER(Weights), vp, vp, vp, sz, vp],
+        "h3dit_block_forward_timed": [cfgp, vp, vp, ctypes.POINTER(Weights), vp, vp, vp, sz, vp,
+                                      ctypes.POINTER(vp), ctypes.c_int],
+        "h3dit_modulation": [cfgp, vp, vp, vp, vp],
+        "h3dit_rmsnorm_modulate": [cfgp, vp, i32, vp, vp, vp, vp],
+        "h3dit_rope_table": [cfgp, vp, vp, vp],
+        "h3dit_qkv_rope": [cfgp, vp, vp, vp, vp, vp, vp],
+        "h3dit_attention": [cfgp, vp, vp, vp, vp],
+        "h3dit_out_proj_residual": [cfgp, vp, vp, vp, i32, vp, vp, vp],
+        "h3dit_mlp_up_gelu": [cfgp, vp, vp, vp, vp],
+        "h3dit_mlp_down_residual": [cfgp, vp, vp, vp, vp, vp, vp],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.h3dit_padded_tokens.argtypes = [ctypes.c_int64]
+    lib.h3dit_padded_tokens.restype = ctypes.c_int64
+    lib.h3dit_status_string.argtypes = [ctypes.c_int]
+    lib.h3dit_status_string.restype = ctypes.c_char_p
+    lib.h3dit_last_error.argtypes = []
+    lib.h3dit_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int, name: str) -> None:
+    if status != H3DIT_OK:
+        detail = load_library().h3dit_last_error().decode()
+        raise H3ditError(status, name, detail)
+
+
+def make_config(hidden: int, heads: int, ffn: int, n_tokens: int, x_dtype: int = H3DIT_BF16,
+                eps: float = 1e-6, rope_base: float = 10000.0, head_dim: int = 128) -> Config:
+    return Config(hidden, heads, head_dim, ffn, n_tokens, x_dtype, eps, rope_base)
+
+
+def config_from(block_cfg) -> Config:
+    """Config for a joint_attention_dit_amd.inputs.BlockConfig."""
+    return make_config(block_cfg.hidden, block_cfg.heads, block_cfg.ffn, block_cfg.n_tokens,
+                       H3DIT_F32 if block_cfg.x_dtype == "fp32" else H3DIT_BF16,
+                       block_cfg.eps, block_cfg.rope_base, block_cfg.head_dim)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return H3DIT_BF16
+    if t.dtype == torch.float32:
+        return H3DIT_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------ ABI calls
+def h3dit_workspace_size(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().h3dit_workspace_size(ctypes.byref(cfg), ctypes.byref(n)),
+           "h3dit_workspace_size")
+    return n.value
+
+
+def h3dit_padded_tokens(n_tokens: int) -> int:
+    return int(load_library().h3dit_padded_tokens(n_tokens))
+
+
+def weights_struct(w: Dict[str, torch.Tensor]) -> Weights:
+    return Weights(_ptr(w["w_ada"]), _ptr(w["w_qkv"]), _ptr(w["w_o"]), _ptr(w["w_up"]),
+                   _ptr(w["w_down"]))
+
+
+def h3dit_block_forward(cfg: Config, x: torch.Tensor, cond: torch.Tensor,
+                        w: Dict[str, torch.Tensor], positions: torch.Tensor, out: torch.Tensor,
+                        workspace: torch.Tensor, stream=None) -> None:
+    ws = weights_struct(w)
+    _check(load_library().h3dit_block_forward(
+        ctypes.byref(cfg), _ptr(x), _ptr(cond), ctypes.byref(ws), _ptr(positions), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+        "h3dit_block_forward")
+
+
+def h3dit_block_forward_timed(cfg: Config, x, cond, w, positions, out, workspace,
+                              events: Sequence[int], stream=None) -> None:
+    ws = weights_struct(w)
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(load_library().h3dit_block_forward_timed(
+        ctypes.byref(cfg), _ptr(x), _ptr(cond), ctypes.byref(ws), _ptr(positions), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream),
+        arr, len(events)), "h3dit_block_forward_timed")
+
+
+def h3dit_modulation(cfg: Config, w_ada, cond, mod, stream=None) -> None:
+    _check(load_library().h3dit_modulation(ctypes.byref(cfg), _ptr(w_ada), _ptr(cond), _ptr(mod),
+                                           _stream(stream)), "h3dit_modulation")
+
+
+def h3dit_rmsnorm_modulate(cfg: Config, x, shift, scale, h, stream=None) -> None:
+    _check(load_library().h3dit_rmsnorm_modulate(ctypes.byref(cfg), _ptr(x), _dtype_code(x),
+                                                 _ptr(shift), _ptr(scale), _ptr(h),
+                                                 _stream(stream)), "h3dit_rmsnorm_modulate")
+
+
+def h3dit_rope_table(cfg: Config, positions, table, stream=None) -> None:
+    _check(load_library().h3dit_rope_table(ctypes.byref(cfg), _ptr(positions), _ptr(table),
+                                           _stream(stream)), "h3dit_rope_table")
+
+
+def h3dit_qkv_rope(cfg: Config, h, w_qkv, table, qk, vt, stream=None) -> None:
+    _check(load_library().h3dit_qkv_rope(ctypes.byref(cfg), _ptr(h), _ptr(w_qkv), _ptr(table),
+                                         _ptr(qk), _ptr(vt), _stream(stream)), "h3dit_qkv_rope")
+
+
+def h3dit_attention(cfg: Config, qk, vt, o, stream=None) -> None:
+    _check(load_library().h3dit_attention(ctypes.byref(cfg), _ptr(qk), _ptr(vt), _ptr(o),
+                                          _stream(stream)), "h3dit_attention")
+
+
+def h3dit_out_proj_residual(cfg: Config, o, w_o, resid, gate, x1, stream=None) -> None:
+    _check(load_library().h3dit_out_proj_residual(ctypes.byref(cfg), _ptr(o), _ptr(w_o),
+                                                  _ptr(resid), _dtype_code(resid), _ptr(gate),
+                                                  _ptr(x1), _stream(stream)),
+           "h3dit_out_proj_residual")
+
+
+def h3dit_mlp_up_gelu(cfg: Config, h2, w_up, u, stream=None) -> None:
+    _check(load_library().h3dit_mlp_up_gelu(ctypes.byref(cfg), _ptr(h2), _ptr(w_up), _ptr(u),
+                                            _stream(stream)), "h3dit_mlp_up_gelu")
+
+
+def h3dit_mlp_down_residual(cfg: Config, u, w_down, x1, gate, out, stream=None) -> None:
+    _check(load_library().h3dit_mlp_down_residual(ctypes.byref(cfg), _ptr(u), _ptr(w_down),
+                                                  _ptr(x1), _ptr(gate), _ptr(out),
+                                                  _stream(stream)), "h3dit_mlp_down_residual")
+
+
+# ------------------------------------------------------------------ helpers
+class Block:
+    """Device-resident inputs + workspace for repeated h3dit_block_forward calls."""
+
+    def __init__(self, block_cfg, inputs: Dict[str, torch.Tensor], device: str = "cuda"):
+        self.block_cfg = block_cfg
+        self.cfg = config_from(block_cfg)
+        self.dev = {k: v.to(device).contiguous() for k, v in inputs.items()}
+        self.weights = {k: self.dev[k] for k in ("w_ada", "w_qkv", "w_o", "w_up", "w_down")}
+        T, D = block_cfg.n_tokens, block_cfg.hidden
+        self.out = torch.empty(T, D, dtype=torch.float32, device=device)
+        nbytes = h3dit_workspace_size(self.cfg)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+    def forward(self, stream=None) -> torch.Tensor:
+        d = self.dev
+        h3dit_block_forward(self.cfg, d["x"], d["cond"], self.weights, d["positions"], self.out,
+                            self.workspace, stream)
+        return self.out
+
+    def forward_timed(self, events: Sequence[int], stream=None) -> torch.Tensor:
+        d = self.dev
+        h3dit_block_forward_timed(self.cfg, d["x"], d["cond"], self.weights, d["positions"],
+                                  self.out, self.workspace, events, stream)
+        return self.out

@@ -1,0 +1,45 @@
+// Shared device types and helpers for the gfx950 kernels of the DiT block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3dit {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// log2(e) / sqrt(128): turns a q.k dot product into a base-2 softmax exponent.
+constexpr float kLog2eOverSqrt128 = (float)(1.4426950408889634 / 11.313708498984761);
+
+// Round-to-nearest-even conversions (gfx950 converts f32 pairs in hardware;
+// the f64 path rounds to odd first, so it is a single correct rounding).
+__device__ __forceinline__ bf16 to_bf16(float v) { return (bf16)v; }
+__device__ __forceinline__ bf16 to_bf16(double v) { return (bf16)v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+__device__ __forceinline__ bf16x2 pack2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_convertvector(v, bf16x2);
+}
+
+__device__ __forceinline__ float bf16_round_f32(float v) { return (float)(bf16)v; }
+
+// 32x32x16 bf16 matrix-core product with fp32 accumulation.
+// Lane l supplies A[l % 32][8 * (l / 32) .. +7] and B[8 * (l / 32) .. +7][l % 32];
+// it receives C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32] in element i.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace h3dit

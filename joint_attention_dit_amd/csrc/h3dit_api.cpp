@@ -1,0 +1,398 @@
+// C ABI of the DiT block library: argument validation, workspace plan and the
+// order in which the block's kernels are enqueued (apxml.com spec page,
+// "Architecture Diagram": modulation, RMSNorm, attention, residual,
+// modulation, RMSNorm, GELU MLP, residual).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/h3dit.h"
+#include "kernels.h"
+
+using namespace h3dit;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return H3DIT_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(H3DIT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Test hook: H3DIT_FAULT_INJECT=launch makes every launch report failure
+// before anything is enqueued, so the error path can be exercised on a host.
+bool fault_injected() {
+  const char *v = getenv("H3DIT_FAULT_INJECT");
+  return v && strcmp(v, "launch") == 0;
+}
+
+int check_config(const h3dit_config *cfg) {
+  if (!cfg) return fail(H3DIT_EINVAL, "cfg is NULL");
+  if (cfg->head_dim != 128)
+    return fail(H3DIT_EUNSUPPORTED, "head_dim must be 128 (got %d)", cfg->head_dim);
+  if (cfg->heads < 1) return fail(H3DIT_EINVAL, "heads must be >= 1 (got %d)", cfg->heads);
+  if (cfg->hidden < 64 || cfg->hidden % 64 != 0 || cfg->hidden > 65536)
+    return fail(H3DIT_EUNSUPPORTED, "hidden must be a multiple of 64 in [64, 65536] (got %d)",
+                cfg->hidden);
+  if (cfg->ffn < 64 || cfg->ffn % 64 != 0 || cfg->ffn > 262144)
+    return fail(H3DIT_EUNSUPPORTED, "ffn must be a multiple of 64 in [64, 262144] (got %d)",
+                cfg->ffn);
+  if ((int64_t)cfg->heads * 128 > 65536)
+    return fail(H3DIT_EUNSUPPORTED, "heads * 128 must be <= 65536 (got %d heads)", cfg->heads);
+  if (cfg->n_tokens < 1 || cfg->n_tokens > (1 << 20))
+    return fail(H3DIT_EINVAL, "n_tokens must be in [1, 1048576] (got %d)", cfg->n_tokens);
+  if (cfg->x_dtype != H3DIT_BF16 && cfg->x_dtype != H3DIT_F32)
+    return fail(H3DIT_EINVAL, "x_dtype must be H3DIT_BF16 or H3DIT_F32 (got %d)", cfg->x_dtype);
+  if (!(cfg->eps >= 0.0f) || !(cfg->eps < 1.0f))
+    return fail(H3DIT_EINVAL, "eps must be in [0, 1)");
+  if (!(cfg->rope_base > 1.0f) || !(cfg->rope_base < 1e30f))
+    return fail(H3DIT_EINVAL, "rope_base must be > 1");
+  return H3DIT_OK;
+}
+
+#define CHECK_PTR(p)                                                        \
+  do {                                                                      \
+    if (!(p)) return fail(H3DIT_EINVAL, "%s is NULL", #p);                  \
+    if (!aligned16(p)) return fail(H3DIT_EALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+#define CHECK_CFG(cfg)                  \
+  do {                                  \
+    const int st_ = check_config(cfg);  \
+    if (st_ != H3DIT_OK) return st_;    \
+  } while (0)
+
+#define LAUNCH(expr, what)                                          \
+  do {                                                              \
+    if (fault_injected()) return fail(H3DIT_EHIP, "%s: injected launch fault", what); \
+    const hipError_t e_ = (expr);                                   \
+    if (e_ != hipSuccess) return hip_fail(e_, what);                \
+  } while (0)
+
+struct Plan {
+  int64_t T, D, A, H, F, Tp;
+  size_t mod, table, h, qk, vt, o, x1, u, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Plan make_plan(const h3dit_config *c) {
+  Plan p;
+  p.T = c->n_tokens;
+  p.D = c->hidden;
+  p.H = c->heads;
+  p.A = p.H * 128;
+  p.F = c->ffn;
+  p.Tp = h3dit_padded_tokens(p.T);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  p.mod = take(sizeof(double) * 6 * p.D);
+  p.table = take(sizeof(float) * 128 * p.T);
+  p.h = take(2 * p.T * p.D);
+  p.qk = take(2 * p.T * 2 * p.A);
+  p.vt = take(2 * p.A * p.Tp);
+  p.o = take(2 * p.T * p.A);
+  p.x1 = take(4 * p.T * p.D);
+  p.u = take(2 * p.T * p.F);
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T *at(void *base, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(base) + off);
+}
+
+GemmArgs gemm_args(const void *x, const void *w, int64_t M, int64_t N, int64_t K) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.x = x;
+  g.w = w;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  return g;
+}
+
+int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, const h3dit_weights *w,
+                 const int32_t *positions, float *out, void *ws, size_t ws_bytes, void *stream,
+                 void *const *events, int n_events) {
+  CHECK_CFG(cfg);
+  if (!w) return fail(H3DIT_EINVAL, "w is NULL");
+  CHECK_PTR(x);
+  CHECK_PTR(cond);
+  CHECK_PTR(positions);
+  CHECK_PTR(out);
+  CHECK_PTR(ws);
+  CHECK_PTR(w->w_ada);
+  CHECK_PTR(w->w_qkv);
+  CHECK_PTR(w->w_o);
+  CHECK_PTR(w->w_up);
+  CHECK_PTR(w->w_down);
+  if (events) {
+    if (n_events != 10) return fail(H3DIT_EINVAL, "n_events must be 10 (got %d)", n_events);
+    for (int i = 0; i < 10; ++i)
+      if (!events[i]) return fail(H3DIT_EINVAL, "events[%d] is NULL", i);
+  }
+  const Plan p = make_plan(cfg);
+  if (ws_bytes < p.total)
+    return fail(H3DIT_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.total);
+  {
+    const size_t xb = (cfg->x_dtype == H3DIT_F32 ? 4 : 2) * (size_t)(p.T * p.D);
+    const size_t ob = 4 * (size_t)(p.T * p.D);
+    const char *xs = static_cast<const char *>(x), *os = reinterpret_cast<const char *>(out);
+    const char *wss = static_cast<const char *>(ws);
+    if (os < xs + xb && xs < os + ob) return fail(H3DIT_EINVAL, "out overlaps x");
+    if (os < wss + p.total && wss < os + ob) return fail(H3DIT_EINVAL, "out overlaps workspace");
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double *mod = at<double>(ws, p.mod);
+  float *table = at<float>(ws, p.table);
+  void *h = at<void>(ws, p.h);
+  void *qk = at<void>(ws, p.qk);
+  void *vt = at<void>(ws, p.vt);
+  void *o = at<void>(ws, p.o);
+  float *x1 = at<float>(ws, p.x1);
+  void *u = at<void>(ws, p.u);
+  const int T = (int)p.T, D = (int)p.D, A = (int)p.A, F = (int)p.F, H = (int)p.H;
+
+  auto mark = [&](int i) -> hipError_t {
+    if (!events) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+  };
+
+  LAUNCH(mark(0), "event record");
+  LAUNCH(launch_modulation(w->w_ada, cond, mod, 6 * D, D, s), "modulation");
+  LAUNCH(mark(1), "event record");
+  LAUNCH(launch_rope_table(positions, table, T, cfg->rope_base, s), "rope table");
+  LAUNCH(mark(2), "event record");
+  LAUNCH(launch_rmsnorm_modulate(x, cfg->x_dtype == H3DIT_F32, mod + 0 * D, mod + 1 * D, h, T, D,
+                                 cfg->eps, s),
+         "rmsnorm 1");
+  LAUNCH(mark(3), "event record");
+  {
+    GemmArgs g = gemm_args(h, w->w_qkv, T, 3 * (int64_t)A, D);
+    g.out = qk;
+    g.out2 = vt;
+    g.table = table;
+    g.A = A;
+    g.Mp = (int)p.Tp;
+    LAUNCH(launch_gemm(EPI_QKV_ROPE, g, s), "qkv gemm");
+  }
+  LAUNCH(mark(4), "event record");
+  LAUNCH(launch_attention(qk, vt, o, T, H, (int)p.Tp, s), "attention");
+  LAUNCH(mark(5), "event record");
+  {
+    GemmArgs g = gemm_args(o, w->w_o, T, D, A);
+    g.out = x1;
+    g.resid = x;
+    g.gate = mod + 2 * D;
+    LAUNCH(launch_gemm(cfg->x_dtype == H3DIT_F32 ? EPI_RESID_F32 : EPI_RESID_BF16, g, s),
+           "output projection");
+  }
+  LAUNCH(mark(6), "event record");
+  LAUNCH(launch_rmsnorm_modulate(x1, true, mod + 3 * D, mod + 4 * D, h, T, D, cfg->eps, s),
+         "rmsnorm 2");
+  LAUNCH(mark(7), "event record");
+  {
+    GemmArgs g = gemm_args(h, w->w_up, T, F, D);
+    g.out = u;
+    LAUNCH(launch_gemm(EPI_GELU, g, s), "mlp up");
+  }
+  LAUNCH(mark(8), "event record");
+  {
+    GemmArgs g = gemm_args(u, w->w_down, T, D, F);
+    g.out = out;
+    g.resid = x1;
+    g.gate = mod + 5 * D;
+    LAUNCH(launch_gemm(EPI_RESID_F32, g, s), "mlp down");
+  }
+  LAUNCH(mark(9), "event record");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t h3dit_padded_tokens(int64_t n_tokens) { return (n_tokens + 63) / 64 * 64; }
+
+int h3dit_workspace_size(const h3dit_config *cfg, size_t *bytes) {
+  CHECK_CFG(cfg);
+  if (!bytes) return fail(H3DIT_EINVAL, "bytes is NULL");
+  *bytes = make_plan(cfg).total;
+  return ok();
+}
+
+int h3dit_block_forward(const h3dit_config *cfg, const void *x, const float *cond,
+                        const h3dit_weights *w, const int32_t *positions, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  return forward_impl(cfg, x, cond, w, positions, out, workspace, workspace_bytes, stream, nullptr,
+                      0);
+}
+
+int h3dit_block_forward_timed(const h3dit_config *cfg, const void *x, const float *cond,
+                              const h3dit_weights *w, const int32_t *positions, float *out,
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              void *const *events, int n_events) {
+  if (!events) return fail(H3DIT_EINVAL, "events is NULL");
+  return forward_impl(cfg, x, cond, w, positions, out, workspace, workspace_bytes, stream, events,
+                      n_events);
+}
+
+int h3dit_modulation(const h3dit_config *cfg, const void *w_ada, const float *cond, double *mod,
+                     void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(w_ada);
+  CHECK_PTR(cond);
+  CHECK_PTR(mod);
+  LAUNCH(launch_modulation(w_ada, cond, mod, 6 * cfg->hidden, cfg->hidden,
+                           static_cast<hipStream_t>(stream)),
+         "modulation");
+  return ok();
+}
+
+int h3dit_rmsnorm_modulate(const h3dit_config *cfg, const void *x, int32_t x_dtype,
+                           const double *shift, const double *scale, void *h, void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(x);
+  CHECK_PTR(shift);
+  CHECK_PTR(scale);
+  CHECK_PTR(h);
+  if (x_dtype != H3DIT_BF16 && x_dtype != H3DIT_F32)
+    return fail(H3DIT_EINVAL, "x_dtype must be H3DIT_BF16 or H3DIT_F32 (got %d)", x_dtype);
+  LAUNCH(launch_rmsnorm_modulate(x, x_dtype == H3DIT_F32, shift, scale, h, cfg->n_tokens,
+                                 cfg->hidden, cfg->eps, static_cast<hipStream_t>(stream)),
+         "rmsnorm");
+  return ok();
+}
+
+int h3dit_rope_table(const h3dit_config *cfg, const int32_t *positions, float *table,
+                     void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(positions);
+  CHECK_PTR(table);
+  LAUNCH(launch_rope_table(positions, table, cfg->n_tokens, cfg->rope_base,
+                           static_cast<hipStream_t>(stream)),
+         "rope table");
+  return ok();
+}
+
+int h3dit_qkv_rope(const h3dit_config *cfg, const void *h, const void *w_qkv, const float *table,
+                   void *qk, void *vt, void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(h);
+  CHECK_PTR(w_qkv);
+  CHECK_PTR(table);
+  CHECK_PTR(qk);
+  CHECK_PTR(vt);
+  const int64_t A = (int64_t)cfg->heads * 128;
+  GemmArgs g = gemm_args(h, w_qkv, cfg->n_tokens, 3 * A, cfg->hidden);
+  g.out = qk;
+  g.out2 = vt;
+  g.table = table;
+  g.A = (int)A;
+  g.Mp = (int)h3dit_padded_tokens(cfg->n_tokens);
+  LAUNCH(launch_gemm(EPI_QKV_ROPE, g, static_cast<hipStream_t>(stream)), "qkv gemm");
+  return ok();
+}
+
+int h3dit_attention(const h3dit_config *cfg, const void *qk, const void *vt, void *o,
+                    void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(qk);
+  CHECK_PTR(vt);
+  CHECK_PTR(o);
+  LAUNCH(launch_attention(qk, vt, o, cfg->n_tokens, cfg->heads,
+                          (int)h3dit_padded_tokens(cfg->n_tokens), static_cast<hipStream_t>(stream)),
+         "attention");
+  return ok();
+}
+
+int h3dit_out_proj_residual(const h3dit_config *cfg, const void *o, const void *w_o,
+                            const void *resid, int32_t resid_dtype, const double *gate, float *x1,
+                            void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(o);
+  CHECK_PTR(w_o);
+  CHECK_PTR(resid);
+  CHECK_PTR(gate);
+  CHECK_PTR(x1);
+  if (resid_dtype != H3DIT_BF16 && resid_dtype != H3DIT_F32)
+    return fail(H3DIT_EINVAL, "resid_dtype must be H3DIT_BF16 or H3DIT_F32 (got %d)", resid_dtype);
+  GemmArgs g = gemm_args(o, w_o, cfg->n_tokens, cfg->hidden, (int64_t)cfg->heads * 128);
+  g.out = x1;
+  g.resid = resid;
+  g.gate = gate;
+  LAUNCH(launch_gemm(resid_dtype == H3DIT_F32 ? EPI_RESID_F32 : EPI_RESID_BF16, g,
+                     static_cast<hipStream_t>(stream)),
+         "output projection");
+  return ok();
+}
+
+int h3dit_mlp_up_gelu(const h3dit_config *cfg, const void *h2, const void *w_up, void *u,
+                      void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(h2);
+  CHECK_PTR(w_up);
+  CHECK_PTR(u);
+  GemmArgs g = gemm_args(h2, w_up, cfg->n_tokens, cfg->ffn, cfg->hidden);
+  g.out = u;
+  LAUNCH(launch_gemm(EPI_GELU, g, static_cast<hipStream_t>(stream)), "mlp up");
+  return ok();
+}
+
+int h3dit_mlp_down_residual(const h3dit_config *cfg, const void *u, const void *w_down,
+                            const float *x1, const double *gate, float *out, void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(u);
+  CHECK_PTR(w_down);
+  CHECK_PTR(x1);
+  CHECK_PTR(gate);
+  CHECK_PTR(out);
+  GemmArgs g = gemm_args(u, w_down, cfg->n_tokens, cfg->hidden, cfg->ffn);
+  g.out = out;
+  g.resid = x1;
+  g.gate = gate;
+  LAUNCH(launch_gemm(EPI_RESID_F32, g, static_cast<hipStream_t>(stream)), "mlp down");
+  return ok();
+}
+
+const char *h3dit_status_string(int status) {
+  switch (status) {
+    case H3DIT_OK: return "H3DIT_OK";
+    case H3DIT_EINVAL: return "H3DIT_EINVAL: invalid argument";
+    case H3DIT_EUNSUPPORTED: return "H3DIT_EUNSUPPORTED: unsupported shape";
+    case H3DIT_EWORKSPACE: return "H3DIT_EWORKSPACE: workspace too small";
+    case H3DIT_EALIGN: return "H3DIT_EALIGN: pointer not 16-byte aligned";
+    case H3DIT_EHIP: return "H3DIT_EHIP: HIP launch failed";
+    default: return "unknown h3dit status";
+  }
+}
+
+const char *h3dit_last_error(void) { return g_last_error; }
+
+}  // extern "C"

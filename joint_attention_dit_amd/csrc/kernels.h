@@ -1,0 +1,44 @@
+// Internal launchers of the gfx950 kernels (C++ linkage, not exported).
+// Each returns the hipError_t of its launch; shapes are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3dit {
+
+// mod[rows] (fp64) = w[rows, cols] (bf16) . cond[cols] (fp32); cols % 8 == 0
+hipError_t launch_modulation(const void *w, const float *cond, double *mod, int rows, int cols,
+                             hipStream_t s);
+
+// h[T, D] (bf16) = bf16(rmsnorm(x) * (1 + scale) + shift), fp64 math; D % 8 == 0
+hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *shift,
+                                   const double *scale, void *h, int T, int D, float eps,
+                                   hipStream_t s);
+
+// table[T, 64] float2 (cos, sin)
+hipError_t launch_rope_table(const int32_t *pos, float *table, int T, float base, hipStream_t s);
+
+enum GemmEpilogue { EPI_QKV_ROPE = 0, EPI_RESID_BF16 = 1, EPI_RESID_F32 = 2, EPI_GELU = 3 };
+
+struct GemmArgs {
+  const void *x;      // B operand rows: activations [M, K] bf16
+  const void *w;      // A operand rows: weights [N, K] bf16
+  int M, N, K;
+  // epilogue operands
+  void *out;          // QKV: qk [M, 2A]; RESID: fp32 [M, N]; GELU: bf16 [M, N]
+  void *out2;         // QKV: vt [H, 128, Mp]
+  const void *resid;  // RESID: [M, N] bf16 or fp32
+  const double *gate; // RESID: [N]
+  const float *table; // QKV: rope table [M, 64] float2
+  int A;              // QKV: attention width
+  int Mp;             // QKV: padded token count of vt
+};
+
+hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s);
+
+// o[T, A] = attention over qk [T, 2A] and vt [H, 128, Tp]
+hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
+                            hipStream_t s);
+
+}  // namespace h3dit

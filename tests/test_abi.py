@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU work is launched).
+
+The library is loaded and every function declared in include/h3dit.h must be
+exported. Argument validation runs on the host before any HIP call, so each
+error path is exercised here with placeholder (never dereferenced) pointers.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from joint_attention_dit_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3dit.h")
+
+# placeholder device addresses: aligned, disjoint, never touched
+P = {name: 0x100000000 * (i + 1) for i, name in enumerate(
+    ["x", "cond", "pos", "out", "ws", "w_ada", "w_qkv", "w_o", "w_up", "w_down", "mod", "h"])}
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3dit_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in h3dit.h but not exported"
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_config_struct_layout():
+    assert ctypes.sizeof(B.Config) == 32
+    assert ctypes.sizeof(B.Weights) == 40
+
+
+def full_cfg(**kw):
+    c = B.make_config(5376, 56, 14336, 16896)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_size_plan():
+    n = B.h3dit_workspace_size(full_cfg())
+    T, D, A, F = 16896, 5376, 7168, 14336
+    Tp = B.h3dit_padded_tokens(T)
+    assert Tp == 16896 and B.h3dit_padded_tokens(288) == 320 and B.h3dit_padded_tokens(1) == 64
+    lower = 6 * D * 8 + 128 * T * 4 + 2 * T * D + 4 * T * A + 2 * A * Tp + 2 * T * A + 4 * T * D + 2 * T * F
+    assert lower <= n <= lower + 8 * 256
+    assert B.h3dit_workspace_size(B.make_config(256, 2, 1024, 1)) > 0
+
+
+def _forward(lib, cfg, ws_bytes=1 << 40, **override):
+    p = dict(P)
+    p.update(override)
+    w = B.Weights(p["w_ada"], p["w_qkv"], p["w_o"], p["w_up"], p["w_down"])
+    return lib.h3dit_block_forward(ctypes.byref(cfg), p["x"], p["cond"], ctypes.byref(w), p["pos"],
+                                   p["out"], p["ws"], ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, B.H3DIT_EUNSUPPORTED),
+    ("hidden", 5377, B.H3DIT_EUNSUPPORTED),
+    ("hidden", 0, B.H3DIT_EUNSUPPORTED),
+    ("ffn", 100, B.H3DIT_EUNSUPPORTED),
+    ("heads", 0, B.H3DIT_EINVAL),
+    ("n_tokens", 0, B.H3DIT_EINVAL),
+    ("n_tokens", (1 << 20) + 1, B.H3DIT_EINVAL),
+    ("x_dtype", 7, B.H3DIT_EINVAL),
+    ("eps", -1.0, B.H3DIT_EINVAL),
+    ("rope_base", 0.0, B.H3DIT_EINVAL),
+])
+def test_config_validation(lib, field, value, status):
+    assert _forward(lib, full_cfg(**{field: value})) == status
+    assert lib.h3dit_last_error().decode() != ""
+
+
+def test_null_misaligned_workspace_overlap(lib):
+    cfg = full_cfg()
+    assert _forward(lib, cfg, x=None) == B.H3DIT_EINVAL
+    assert "x is NULL" in lib.h3dit_last_error().decode()
+    assert _forward(lib, cfg, w_down=0) == B.H3DIT_EINVAL
+    assert _forward(lib, cfg, cond=P["cond"] + 4) == B.H3DIT_EALIGN
+    assert _forward(lib, cfg, ws_bytes=1000) == B.H3DIT_EWORKSPACE
+    assert _forward(lib, cfg, out=P["x"]) == B.H3DIT_EINVAL
+    assert "overlaps" in lib.h3dit_last_error().decode()
+    assert lib.h3dit_block_forward(None, P["x"], P["cond"], None, P["pos"], P["out"], P["ws"],
+                                   1 << 40, None) == B.H3DIT_EINVAL
+
+
+def test_timed_variant_validates_events(lib):
+    cfg = full_cfg()
+    w = B.Weights(P["w_ada"], P["w_qkv"], P["w_o"], P["w_up"], P["w_down"])
+    ev = (ctypes.c_void_p * 10)(*([0x1000] * 10))
+    assert lib.h3dit_block_forward_timed(ctypes.byref(cfg), P["x"], P["cond"], ctypes.byref(w),
+                                         P["pos"], P["out"], P["ws"], 1 << 40, None, ev,
+                                         9) == B.H3DIT_EINVAL
+    ev[3] = None
+    assert lib.h3dit_block_forward_timed(ctypes.byref(cfg), P["x"], P["cond"], ctypes.byref(w),
+                                         P["pos"], P["out"], P["ws"], 1 << 40, None, ev,
+                                         10) == B.H3DIT_EINVAL
+
+
+def test_stage_validation(lib):
+    cfg = full_cfg()
+    assert lib.h3dit_modulation(ctypes.byref(cfg), None, P["cond"], P["mod"], None) == B.H3DIT_EINVAL
+    assert lib.h3dit_rmsnorm_modulate(ctypes.byref(cfg), P["x"], 5, P["mod"], P["mod"], P["h"],
+                                      None) == B.H3DIT_EINVAL
+    assert lib.h3dit_attention(ctypes.byref(full_cfg(head_dim=96)), P["x"], P["x"], P["h"],
+                               None) == B.H3DIT_EUNSUPPORTED
+    assert lib.h3dit_out_proj_residual(ctypes.byref(cfg), P["x"], P["w_o"], P["x"], 3, P["mod"],
+                                       P["out"], None) == B.H3DIT_EINVAL
+
+
+def test_fault_injection_reports_hip_error(lib, monkeypatch):
+    monkeypatch.setenv("H3DIT_FAULT_INJECT", "launch")
+    assert _forward(lib, full_cfg()) == B.H3DIT_EHIP
+    assert "injected" in lib.h3dit_last_error().decode()
+    with pytest.raises(B.H3ditError):
+        B._check(B.H3DIT_EHIP, "h3dit_block_forward")
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.h3dit_status_string(s).startswith(b"H3DIT_")
+    assert b"unknown" in lib.h3dit_status_string(42)

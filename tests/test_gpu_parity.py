@@ -1,0 +1,264 @@
+"""GPU parity of the HIP path against the float64 CPU oracle (contract mode).
+
+Stage tests feed each entry point the oracle's own inputs for that step, so a
+failure names the step. Block tests run h3dit_block_forward end to end and
+compare the output element by element (all rows for small blocks, 256 seeded
+rows for the full-width blocks) against the bar: max |err| <= 2e-2 * RMS(out)
+and relative L2 <= 5e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from joint_attention_dit_amd import binding as B
+from joint_attention_dit_amd.inputs import CONFIGS, make_inputs, sample_rows, small_config
+
+from tests._common import (assert_bf16_close, assert_block_parity, bf16_ulp_diff, cached_case,
+                           errors, oracle_inputs, oracle_reference)
+
+pytestmark = pytest.mark.gpu
+
+MID = small_config("mid", hidden=512, heads=4, ffn=1536, text_tokens=35, images=((23, 29, 0),),
+                   x_dtype="bf16")
+MID32 = small_config("mid32", hidden=384, heads=3, ffn=1024, text_tokens=10, images=((9, 13, 0),),
+                     x_dtype="fp32")
+SMALL_CASES = [CONFIGS["tiny"], MID, MID32]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev(t, dtype=None):
+    t = t if dtype is None else t.to(dtype)
+    return t.contiguous().cuda()
+
+
+def bf16_dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.bfloat16).cuda()
+
+
+def f64_dev(a: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+# ------------------------------------------------------------------ stages
+@pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
+def test_stage_modulation(cfg):
+    inp = cached_case(cfg)
+    say(f"[stage] modulation {cfg.name} D={cfg.hidden}")
+    c = B.config_from(cfg)
+    mod = torch.empty(6 * cfg.hidden, dtype=torch.float64, device="cuda")
+    B.h3dit_modulation(c, dev(inp["w_ada"]), dev(inp["cond"]), mod)
+    x, cond, w, pos = oracle_inputs(inp)
+    np.testing.assert_allclose(host(mod), O.modulation(w["w_ada"], cond), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
+def test_stage_rmsnorm_modulate(cfg):
+    inp = cached_case(cfg)
+    say(f"[stage] rmsnorm {cfg.name} T={cfg.n_tokens} D={cfg.hidden} x={cfg.x_dtype}")
+    x, cond, w, pos = oracle_inputs(inp)
+    mv = O.split_modulation(O.modulation(w["w_ada"], cond), cfg.hidden)
+    c = B.config_from(cfg)
+    h = torch.empty(cfg.n_tokens, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+    B.h3dit_rmsnorm_modulate(c, dev(inp["x"]), f64_dev(mv["shift1"]), f64_dev(mv["scale1"]), h)
+    ref = O.modulated_norm(x, mv["shift1"], mv["scale1"], cfg.eps, "contract")
+    ulp = bf16_ulp_diff(host(h), ref)
+    assert ulp.max() <= 1 and np.mean(ulp > 0) < 1e-3, (ulp.max(), np.mean(ulp > 0))
+
+
+@pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
+def test_stage_rope_table(cfg):
+    inp = cached_case(cfg)
+    say(f"[stage] rope table {cfg.name} T={cfg.n_tokens}")
+    c = B.config_from(cfg)
+    table = torch.empty(cfg.n_tokens, 64, 2, dtype=torch.float32, device="cuda")
+    B.h3dit_rope_table(c, dev(inp["positions"]), table)
+    pos = inp["positions"].numpy().astype(np.float64)
+    theta = O.rope_frequencies(cfg.rope_base)
+    ang = np.concatenate([pos[:, 0:1] * theta[None], pos[:, 1:2] * theta[None]], axis=1)
+    got = host(table)
+    np.testing.assert_allclose(got[..., 0], np.cos(ang), atol=1e-7, rtol=0)
+    np.testing.assert_allclose(got[..., 1], np.sin(ang), atol=1e-7, rtol=0)
+
+
+def _qkv_stage(cfg, inp):
+    x, cond, w, pos = oracle_inputs(inp)
+    mv = O.split_modulation(O.modulation(w["w_ada"], cond), cfg.hidden)
+    h1 = O.modulated_norm(x, mv["shift1"], mv["scale1"], cfg.eps, "contract")
+    c = B.config_from(cfg)
+    T, A = cfg.n_tokens, cfg.attn_width
+    Tp = B.h3dit_padded_tokens(T)
+    table = torch.empty(T, 64, 2, dtype=torch.float32, device="cuda")
+    B.h3dit_rope_table(c, dev(inp["positions"]), table)
+    qk = torch.empty(T, 2 * A, dtype=torch.bfloat16, device="cuda")
+    vt = torch.full((cfg.heads, 128, Tp), float("nan"), dtype=torch.bfloat16, device="cuda")
+    B.h3dit_qkv_rope(c, bf16_dev(h1), dev(inp["w_qkv"]), table, qk, vt)
+    return h1, w, pos, qk, vt
+
+
+@pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
+def test_stage_qkv_rope(cfg):
+    inp = cached_case(cfg)
+    say(f"[stage] qkv+rope {cfg.name} T={cfg.n_tokens}")
+    h1, w, pos, qk, vt = _qkv_stage(cfg, inp)
+    T, A, H = cfg.n_tokens, cfg.attn_width, cfg.heads
+    wq, wk, wv = w["w_qkv"][:A], w["w_qkv"][A:2 * A], w["w_qkv"][2 * A:]
+    q = O.bf16_round(O.apply_rope(O.bf16_round(h1 @ wq.T).reshape(T, H, 128), pos, cfg.rope_base))
+    k = O.bf16_round(O.apply_rope(O.bf16_round(h1 @ wk.T).reshape(T, H, 128), pos, cfg.rope_base))
+    v = O.bf16_round(h1 @ wv.T).reshape(T, H, 128)
+    g_qk = host(qk)
+    g_vt = host(vt)
+    for name, got, ref in (("q", g_qk[:, :A], q.reshape(T, A)), ("k", g_qk[:, A:], k.reshape(T, A)),
+                           ("v", g_vt[:, :, :T].transpose(2, 0, 1).reshape(T, A), v.reshape(T, A))):
+        # a one-ulp difference in a bf16 input of the rotation can cancel into
+        # many ulps of a small output, so q and k errors are measured against
+        # the norm of their rotation pair (which RoPE preserves)
+        if name == "v":
+            assert_bf16_close(got, ref, "v", ulps=1, floor_over_rms=1e-4)
+            continue
+        frac = float(np.mean(got != ref))
+        pair = np.sqrt(ref[:, 0::2] ** 2 + ref[:, 1::2] ** 2).repeat(2, axis=1)
+        rel = np.abs(got - ref) / np.maximum(pair, 1e-30)
+        say(f"  {name}: max |err|/pair-norm {rel.max():.2e}, mismatch fraction {frac:.2e}")
+        assert rel.max() <= 2 ** -7 and frac < 1e-2, (name, rel.max(), frac)
+    assert np.all(g_vt[:, :, T:] == 0.0), "vt padding must be zero"
+
+
+@pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
+def test_stage_attention(cfg):
+    inp = cached_case(cfg)
+    say(f"[stage] attention {cfg.name} T={cfg.n_tokens} H={cfg.heads}")
+    h1, w, pos, qk, vt = _qkv_stage(cfg, inp)
+    T, A, H = cfg.n_tokens, cfg.attn_width, cfg.heads
+    o = torch.empty(T, A, dtype=torch.bfloat16, device="cuda")
+    B.h3dit_attention(B.config_from(cfg), qk, vt, o)
+    g_qk, g_vt = host(qk), host(vt)
+    q = g_qk[:, :A].reshape(T, H, 128)
+    k = g_qk[:, A:].reshape(T, H, 128)
+    v = g_vt[:, :, :T].transpose(2, 0, 1)
+    ref = O.attention(q, k, v, "contract").reshape(T, A)
+    got = host(o)
+    e = errors(got, ref)
+    say(f"  o: rel_l2 {e['rel_l2']:.2e}")
+    assert e["rel_l2"] < 1e-3
+    assert_bf16_close(got, ref, "o", ulps=2, floor_over_rms=1e-3, max_mismatch=2e-2)
+
+
+def test_attention_single_token_returns_v():
+    say("[stage] attention T=1")
+    cfg = small_config("one", hidden=256, heads=2, ffn=256, text_tokens=1, images=())
+    c = B.config_from(cfg)
+    g = torch.Generator().manual_seed(5)
+    qk = (torch.randn(1, 512, generator=g) * 4).to(torch.bfloat16).cuda()
+    vt = torch.zeros(2, 128, 64, dtype=torch.bfloat16)
+    vt[:, :, 0] = torch.randn(2, 128, generator=g).to(torch.bfloat16)
+    vt = vt.cuda()
+    o = torch.empty(1, 256, dtype=torch.bfloat16, device="cuda")
+    B.h3dit_attention(c, qk, vt, o)
+    assert torch.equal(o.cpu(), vt[:, :, 0].reshape(1, 256).cpu())
+
+
+@pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
+def test_stage_projections_and_mlp(cfg):
+    inp = cached_case(cfg)
+    say(f"[stage] out-proj / mlp {cfg.name} T={cfg.n_tokens}")
+    ref = oracle_reference(cfg, inp)
+    mv = O.split_modulation(ref["mod"], cfg.hidden)
+    c = B.config_from(cfg)
+    T, D, F = cfg.n_tokens, cfg.hidden, cfg.ffn
+    x1 = torch.empty(T, D, dtype=torch.float32, device="cuda")
+    B.h3dit_out_proj_residual(c, bf16_dev(ref["o"]), dev(inp["w_o"]), dev(inp["x"]),
+                              f64_dev(mv["gate1"]), x1)
+    e = errors(host(x1), ref["x1"])
+    say(f"  x1: rel_l2 {e['rel_l2']:.2e} max_abs/rms {e['max_abs_over_rms']:.2e}")
+    assert e["rel_l2"] < 1e-5 and e["max_abs_over_rms"] < 1e-4
+
+    u = torch.empty(T, F, dtype=torch.bfloat16, device="cuda")
+    B.h3dit_mlp_up_gelu(c, bf16_dev(ref["h2"]), dev(inp["w_up"]), u)
+    assert_bf16_close(host(u), ref["u"], "u", ulps=1, floor_over_rms=1e-4)
+
+    out = torch.empty(T, D, dtype=torch.float32, device="cuda")
+    B.h3dit_mlp_down_residual(c, bf16_dev(ref["u"]), dev(inp["w_down"]),
+                              torch.from_numpy(ref["x1"]).to(torch.float32).cuda(),
+                              f64_dev(mv["gate2"]), out)
+    e = errors(host(out), ref["out"])
+    say(f"  out: rel_l2 {e['rel_l2']:.2e} max_abs/rms {e['max_abs_over_rms']:.2e}")
+    assert e["rel_l2"] < 1e-5 and e["max_abs_over_rms"] < 1e-4
+
+
+# ------------------------------------------------------------------ whole block
+def run_block(cfg, inp):
+    blk = B.Block(cfg, inp)
+    out = blk.forward()
+    return host(out), blk
+
+
+@pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
+def test_block_small_all_rows(cfg):
+    inp = cached_case(cfg)
+    say(f"[block] {cfg.name} T={cfg.n_tokens} all rows")
+    got, _ = run_block(cfg, inp)
+    ref = oracle_reference(cfg, inp)
+    assert_block_parity(got, ref["out"], f"{cfg.name} out")
+    ex = oracle_reference(cfg, inp, mode="exact")
+    e = errors(got, ex["out"])
+    say(f"  (info) vs exact fp64: rel_l2 {e['rel_l2']:.2e} max_abs/rms {e['max_abs_over_rms']:.2e}")
+
+
+@pytest.mark.parametrize("T_text,grid", [(1, ()), (64, ()), (65, ()), (3, ((1, 1, 0),)),
+                                         (0, ((8, 16, 0),))], ids=["T1", "T64", "T65", "T4", "T128"])
+def test_block_edge_token_counts(T_text, grid):
+    cfg = small_config("edge", hidden=256, heads=2, ffn=512, text_tokens=T_text, images=grid)
+    inp = make_inputs(cfg, seed=11)
+    say(f"[block] edge T={cfg.n_tokens}")
+    got, _ = run_block(cfg, inp)
+    assert_block_parity(got, oracle_reference(cfg, inp)["out"], f"edge T={cfg.n_tokens}")
+
+
+def test_block_zero_gates_return_input_bitwise():
+    cfg = MID
+    inp = dict(cached_case(cfg))
+    D = cfg.hidden
+    w_ada = inp["w_ada"].clone()
+    w_ada[2 * D:3 * D] = 0
+    w_ada[5 * D:6 * D] = 0
+    inp["w_ada"] = w_ada
+    say("[block] zero gates")
+    got, _ = run_block(cfg, inp)
+    assert np.array_equal(got, inp["x"].to(torch.float64).numpy())
+
+
+def test_block_deterministic():
+    cfg = MID
+    inp = cached_case(cfg)
+    say("[block] determinism")
+    blk = B.Block(cfg, inp)
+    a = blk.forward().clone()
+    b = blk.forward().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+FULL = ["2048", "nonsquare", "4096", "edit"]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", FULL)
+def test_block_full_width_sampled_rows(name):
+    cfg = CONFIGS[name]
+    say(f"[block] {name} T={cfg.n_tokens} D={cfg.hidden} (256 sampled rows)")
+    inp = make_inputs(cfg, seed=0)
+    got, blk = run_block(cfg, inp)
+    del blk
+    torch.cuda.empty_cache()
+    rows = sample_rows(cfg.n_tokens, 256, seed=1)
+    ref = oracle_reference(cfg, inp, rows=rows)
+    assert_block_parity(got[rows], ref["out"], f"{name} out")
