@@ -163,6 +163,13 @@ int h3dit_mlp_up_gelu(const h3dit_config *cfg, const void *h2, const void *w_up,
 int h3dit_mlp_down_residual(const h3dit_config *cfg, const void *u, const void *w_down,
                             const float *x1, const double *gate, float *out, void *stream);
 
+/* The matrix-core GEMM that the four projections share, with a plain fp32
+ * epilogue (for tests and profiling):
+ *   y[M, N] fp32 = x[M, K] (bf16) . w[N, K]^T (bf16), fp32 accumulation.
+ * Requirements: M, N >= 1; K a positive multiple of 64. */
+int h3dit_linear_f32(const void *x, const void *w, int32_t M, int32_t N, int32_t K, float *y,
+                     void *stream);
+
 /* Padded token count used by the vt layout (T rounded up to a multiple of 64). */
 int64_t h3dit_padded_tokens(int64_t n_tokens);
 

@@ -25,7 +25,7 @@ EXPORTED = (
     "h3dit_workspace_size", "h3dit_block_forward", "h3dit_block_forward_timed",
     "h3dit_modulation", "h3dit_rmsnorm_modulate", "h3dit_rope_table", "h3dit_qkv_rope",
     "h3dit_attention", "h3dit_out_proj_residual", "h3dit_mlp_up_gelu",
-    "h3dit_mlp_down_residual", "h3dit_padded_tokens", "h3dit_status_string",
+    "h3dit_mlp_down_residual", "h3dit_linear_f32", "h3dit_padded_tokens", "h3dit_status_string",
     "h3dit_last_error",
 )
 
@@ -75,6 +75,7 @@ def load_library() -> ctypes.CDLL:
         "h3dit_out_proj_residual": [cfgp, vp, vp, vp, i32, vp, vp, vp],
         "h3dit_mlp_up_gelu": [cfgp, vp, vp, vp, vp],
         "h3dit_mlp_down_residual": [cfgp, vp, vp, vp, vp, vp, vp],
+        "h3dit_linear_f32": [vp, vp, i32, i32, i32, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -211,6 +212,13 @@ def h3dit_mlp_down_residual(cfg: Config, u, w_down, x1, gate, out, stream=None) 
     _check(load_library().h3dit_mlp_down_residual(ctypes.byref(cfg), _ptr(u), _ptr(w_down),
                                                   _ptr(x1), _ptr(gate), _ptr(out),
                                                   _stream(stream)), "h3dit_mlp_down_residual")
+
+
+def h3dit_linear_f32(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    M, K = x.shape
+    N = w.shape[0]
+    _check(load_library().h3dit_linear_f32(_ptr(x), _ptr(w), M, N, K, _ptr(y), _stream(stream)),
+           "h3dit_linear_f32")
 
 
 # ------------------------------------------------------------------ helpers

@@ -115,6 +115,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[
           ov[2] = rv[2] + (float)a.gate[n + 2] * v2;
           ov[3] = rv[3] + (float)a.gate[n + 3] * v3;
           *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + off) = ov;
+        } else if constexpr (EPI == EPI_F32) {
+          if (t >= a.M) continue;
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (int64_t)t * a.N + n) =
+              f32x4{v0, v1, v2, v3};
         } else {  // EPI_GELU
           if (t >= a.M) continue;
           bf16x4 r;
@@ -237,6 +241,9 @@ hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s) {
       break;
     case EPI_GELU:
       hipLaunchKernelGGL(gemm_kernel<EPI_GELU>, dim3(tiles), dim3(256), 0, s, a);
+      break;
+    case EPI_F32:
+      hipLaunchKernelGGL(gemm_kernel<EPI_F32>, dim3(tiles), dim3(256), 0, s, a);
       break;
   }
   return hipGetLastError();

@@ -381,6 +381,20 @@ int h3dit_mlp_down_residual(const h3dit_config *cfg, const void *u, const void *
   return ok();
 }
 
+int h3dit_linear_f32(const void *x, const void *w, int32_t M, int32_t N, int32_t K, float *y,
+                     void *stream) {
+  CHECK_PTR(x);
+  CHECK_PTR(w);
+  CHECK_PTR(y);
+  if (M < 1 || N < 1 || K < 64 || K % 64 != 0 || N % 4 != 0)
+    return fail(H3DIT_EUNSUPPORTED, "linear: need M, N >= 1, N %% 4 == 0, K a multiple of 64 "
+                "(got M=%d N=%d K=%d)", M, N, K);
+  GemmArgs g = gemm_args(x, w, M, N, K);
+  g.out = y;
+  LAUNCH(launch_gemm(EPI_F32, g, static_cast<hipStream_t>(stream)), "linear");
+  return ok();
+}
+
 const char *h3dit_status_string(int status) {
   switch (status) {
     case H3DIT_OK: return "H3DIT_OK";

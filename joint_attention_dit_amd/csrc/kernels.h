@@ -19,14 +19,14 @@ hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *s
 // table[T, 64] float2 (cos, sin)
 hipError_t launch_rope_table(const int32_t *pos, float *table, int T, float base, hipStream_t s);
 
-enum GemmEpilogue { EPI_QKV_ROPE = 0, EPI_RESID_BF16 = 1, EPI_RESID_F32 = 2, EPI_GELU = 3 };
+enum GemmEpilogue { EPI_QKV_ROPE = 0, EPI_RESID_BF16 = 1, EPI_RESID_F32 = 2, EPI_GELU = 3, EPI_F32 = 4 };
 
 struct GemmArgs {
   const void *x;      // B operand rows: activations [M, K] bf16
   const void *w;      // A operand rows: weights [N, K] bf16
   int M, N, K;
   // epilogue operands
-  void *out;          // QKV: qk [M, 2A]; RESID: fp32 [M, N]; GELU: bf16 [M, N]
+  void *out;          // QKV: qk [M, 2A]; RESID, F32: fp32 [M, N]; GELU: bf16 [M, N]
   void *out2;         // QKV: vt [H, 128, Mp]
   const void *resid;  // RESID: [M, N] bf16 or fp32
   const double *gate; // RESID: [N]

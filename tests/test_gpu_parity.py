@@ -245,20 +245,3 @@ def test_block_deterministic():
     b = blk.forward().clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-
-
-FULL = ["2048", "nonsquare", "4096", "edit"]
-
-
-@pytest.mark.slow
-@pytest.mark.parametrize("name", FULL)
-def test_block_full_width_sampled_rows(name):
-    cfg = CONFIGS[name]
-    say(f"[block] {name} T={cfg.n_tokens} D={cfg.hidden} (256 sampled rows)")
-    inp = make_inputs(cfg, seed=0)
-    got, blk = run_block(cfg, inp)
-    del blk
-    torch.cuda.empty_cache()
-    rows = sample_rows(cfg.n_tokens, 256, seed=1)
-    ref = oracle_reference(cfg, inp, rows=rows)
-    assert_block_parity(got[rows], ref["out"], f"{name} out")
