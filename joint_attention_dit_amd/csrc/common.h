@@ -39,6 +39,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 matrix-core product with fp32 accumulation.
+// Lane l supplies A[l % 16][8 * (l / 16) .. +7] and B[8 * (l / 16) .. +7][l % 16];
+// it receives C[4 * (l / 16) + i][l % 16] in element i.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 

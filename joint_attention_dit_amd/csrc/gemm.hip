@@ -10,13 +10,16 @@
 // features of one token: RoPE pairs (2i, 2i+1) sit in one lane and stores are
 // 8- or 16-byte vectors.
 //
-// Tiling: 256 features x 256 tokens per workgroup, K step 64, four waves in a
-// 2 x 2 arrangement, each owning 128 x 128 outputs (4 x 4 MFMA blocks, 256
-// fp32 accumulators per lane). Tiles are staged through LDS, double
-// buffered (2 stages x 2 operands x 32 KB), with a register prefetch of the
-// next K step while the current one is multiplied. LDS rows are 128 bytes;
-// 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7) so that the
-// 32 rows read by one fragment load spread over all banks.
+// Tiling: 256 features x 256 tokens per workgroup, K step 32 (two MFMA
+// k-steps of 16), four waves in a 2 x 2 arrangement, each owning 128 x 128
+// outputs (4 x 4 blocks of 32 x 32, 256 fp32 accumulators per lane).
+// Global tiles go straight into LDS (gfx950's 16-byte global-load-to-LDS)
+// through a 4-stage ring, three tiles ahead of the multiply, with one barrier
+// per K step. The fragments of the second k-step are read from LDS while the
+// first k-step's MFMAs run, and the next tile's first fragments while the
+// second k-step's run. LDS rows are 128 bytes; 16-byte chunk c of row r is
+// stored at chunk c ^ ((r >> 1) & 7), so the 16 rows read by a quarter-wave
+// fragment load cover all 64 banks.
 //
 // Workgroup order: the dispatcher hands workgroup i to XCD i % 8. The
 // linear id is remapped so that each XCD receives a contiguous range of
@@ -25,17 +28,22 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace h3dit {
 
 namespace {
 
 constexpr int BN = 256;   // weight rows (output features) per tile
 constexpr int BT = 256;   // activation rows (tokens) per tile
-constexpr int BK = 64;    // K per LDS stage
-constexpr int TILE_ELEMS = 256 * BK;  // one operand tile, bf16 elements
+constexpr int BK = 32;    // K per LDS stage
+constexpr int NSTAGE = 4; // LDS stages (tiles in flight: NSTAGE - 1 ahead)
+constexpr int TILE_ELEMS = 256 * BK;  // one operand tile, bf16 elements (16 KB)
 constexpr int GROUP_T = 8;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+// LDS rows are 64 bytes (4 chunks of 16 B); 4 rows share one 256-byte bank line,
+// so chunk c of row r is stored at chunk c ^ ((r >> 2) & 3).
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
 
 __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_n, int tiles_t,
                                             int &tn, int &tt) {
@@ -59,123 +67,131 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z / (1.0f + expf(-2.0f * y));
 }
 
+// Four consecutive outputs (features n .. n+3 of token t) through the epilogue.
 template <int EPI>
-__device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x16 (&acc)[4][4], int n_base,
-                                         int t_base, int lane) {
-  const int G = lane >> 5, c = lane & 31;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t_base + j * 32 + c;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n_base + i * 32 + 8 * g + 4 * G;
-        if (n >= a.N) continue;
-        const float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
-        const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-        if constexpr (EPI == EPI_QKV_ROPE) {
-          const int A2 = 2 * a.A;
-          if (n < A2) {
-            if (t >= a.M) continue;
-            // q or k: round, rotate the two adjacent pairs, round again
-            const float u0 = bf16_round_f32(v0), w0 = bf16_round_f32(v1);
-            const float u1 = bf16_round_f32(v2), w1 = bf16_round_f32(v3);
-            const int p = (n & 127) >> 1;  // pair index within the head (0..63)
-            const f32x4 cs = *reinterpret_cast<const f32x4 *>(a.table + ((int64_t)t * 64 + p) * 2);
-            bf16x4 r;
-            r[0] = to_bf16(u0 * cs[0] - w0 * cs[1]);
-            r[1] = to_bf16(u0 * cs[1] + w0 * cs[0]);
-            r[2] = to_bf16(u1 * cs[2] - w1 * cs[3]);
-            r[3] = to_bf16(u1 * cs[3] + w1 * cs[2]);
-            *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * A2 + n) = r;
-          } else {
-            if (t >= a.Mp) continue;
-            const int hv = n - A2;  // head * 128 + dim
-            bf16 *vt = static_cast<bf16 *>(a.out2) + (int64_t)hv * a.Mp + t;
-            const bool live = t < a.M;
-            vt[0] = to_bf16(live ? v0 : 0.0f);
-            vt[a.Mp] = to_bf16(live ? v1 : 0.0f);
-            vt[2 * (int64_t)a.Mp] = to_bf16(live ? v2 : 0.0f);
-            vt[3 * (int64_t)a.Mp] = to_bf16(live ? v3 : 0.0f);
-          }
-        } else if constexpr (EPI == EPI_RESID_BF16 || EPI == EPI_RESID_F32) {
-          if (t >= a.M) continue;
-          const int64_t off = (int64_t)t * a.N + n;
-          f32x4 rv;
-          if constexpr (EPI == EPI_RESID_BF16) {
-            const bf16x4 rb = *reinterpret_cast<const bf16x4 *>(static_cast<const bf16 *>(a.resid) + off);
-            rv = f32x4{(float)rb[0], (float)rb[1], (float)rb[2], (float)rb[3]};
-          } else {
-            rv = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.resid) + off);
-          }
-          f32x4 ov;
-          ov[0] = rv[0] + (float)a.gate[n + 0] * v0;
-          ov[1] = rv[1] + (float)a.gate[n + 1] * v1;
-          ov[2] = rv[2] + (float)a.gate[n + 2] * v2;
-          ov[3] = rv[3] + (float)a.gate[n + 3] * v3;
-          *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + off) = ov;
-        } else if constexpr (EPI == EPI_F32) {
-          if (t >= a.M) continue;
-          *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (int64_t)t * a.N + n) =
-              f32x4{v0, v1, v2, v3};
-        } else {  // EPI_GELU
-          if (t >= a.M) continue;
-          bf16x4 r;
-          r[0] = to_bf16(gelu_tanh(v0));
-          r[1] = to_bf16(gelu_tanh(v1));
-          r[2] = to_bf16(gelu_tanh(v2));
-          r[3] = to_bf16(gelu_tanh(v3));
-          *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * a.N + n) = r;
-        }
-      }
+__device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0, float v1,
+                                       float v2, float v3) {
+  if (n >= a.N) return;
+  if constexpr (EPI == EPI_QKV_ROPE) {
+    const int A2 = 2 * a.A;
+    if (n < A2) {
+      if (t >= a.M) return;
+      // q or k: round, rotate the two adjacent pairs, round again
+      const float u0 = bf16_round_f32(v0), w0 = bf16_round_f32(v1);
+      const float u1 = bf16_round_f32(v2), w1 = bf16_round_f32(v3);
+      const int p = (n & 127) >> 1;  // pair index within the head (0..63)
+      const f32x4 cs = *reinterpret_cast<const f32x4 *>(a.table + ((int64_t)t * 64 + p) * 2);
+      bf16x4 r;
+      r[0] = to_bf16(u0 * cs[0] - w0 * cs[1]);
+      r[1] = to_bf16(u0 * cs[1] + w0 * cs[0]);
+      r[2] = to_bf16(u1 * cs[2] - w1 * cs[3]);
+      r[3] = to_bf16(u1 * cs[3] + w1 * cs[2]);
+      *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * A2 + n) = r;
+    } else {
+      if (t >= a.Mp) return;
+      const int hv = n - A2;  // head * 128 + dim
+      bf16 *vt = static_cast<bf16 *>(a.out2) + (int64_t)hv * a.Mp + t;
+      const bool live = t < a.M;
+      vt[0] = to_bf16(live ? v0 : 0.0f);
+      vt[a.Mp] = to_bf16(live ? v1 : 0.0f);
+      vt[2 * (int64_t)a.Mp] = to_bf16(live ? v2 : 0.0f);
+      vt[3 * (int64_t)a.Mp] = to_bf16(live ? v3 : 0.0f);
     }
+  } else if constexpr (EPI == EPI_RESID_BF16 || EPI == EPI_RESID_F32) {
+    if (t >= a.M) return;
+    const int64_t off = (int64_t)t * a.N + n;
+    f32x4 rv;
+    if constexpr (EPI == EPI_RESID_BF16) {
+      const bf16x4 rb = *reinterpret_cast<const bf16x4 *>(static_cast<const bf16 *>(a.resid) + off);
+      rv = f32x4{(float)rb[0], (float)rb[1], (float)rb[2], (float)rb[3]};
+    } else {
+      rv = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.resid) + off);
+    }
+    f32x4 ov;
+    ov[0] = rv[0] + (float)a.gate[n + 0] * v0;
+    ov[1] = rv[1] + (float)a.gate[n + 1] * v1;
+    ov[2] = rv[2] + (float)a.gate[n + 2] * v2;
+    ov[3] = rv[3] + (float)a.gate[n + 3] * v3;
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + off) = ov;
+  } else if constexpr (EPI == EPI_F32) {
+    if (t >= a.M) return;
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (int64_t)t * a.N + n) =
+        f32x4{v0, v1, v2, v3};
+  } else {  // EPI_GELU
+    if (t >= a.M) return;
+    bf16x4 r;
+    r[0] = to_bf16(gelu_tanh(v0));
+    r[1] = to_bf16(gelu_tanh(v1));
+    r[2] = to_bf16(gelu_tanh(v2));
+    r[3] = to_bf16(gelu_tanh(v3));
+    *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * a.N + n) = r;
   }
 }
 
+// Wait until at most N of this wave's global-to-LDS loads are still in flight
+// (they complete in issue order), then meet the other waves: afterwards every
+// wave's earlier loads have landed in LDS. No LDS instruction is waited for:
+// the tiles reach LDS only through these loads.
+template <int N>
+__device__ __forceinline__ void tile_barrier() {
+  // s_waitcnt vmcnt(N) (lgkmcnt and expcnt fields left at their maximum)
+  constexpr int enc = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  __builtin_amdgcn_s_waitcnt(enc);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * TILE_ELEMS];  // 128 KB
+  __shared__ __attribute__((aligned(1024))) bf16 lds[NSTAGE * 2 * TILE_ELEMS];  // 128 KB
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wt = wave >> 1;
   const int tiles_n = (int)ceil_div(a.N, BN), tiles_t = (int)ceil_div(a.M, BT);
   int tn, tt;
   tile_coords(blockIdx.x, gridDim.x, tiles_n, tiles_t, tn, tt);
   const int n0 = tn * BN, t0 = tt * BT;
 
-  // global -> LDS assignment: chunk (tid & 7) of rows (tid >> 3) + 32 j
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const bf16 *wsrc = static_cast<const bf16 *>(a.w);
-  const bf16 *xsrc = static_cast<const bf16 *>(a.x);
-  int64_t woff[8], xoff[8];
-  int soff[8];
+  // global -> LDS without registers: each wave fills 4 blocks of 1 KB (16 rows of
+  // 64 bytes) per operand tile; lane l lands at byte 16 l of its block, i.e. at
+  // row 16 b + l / 4, physical chunk l % 4, so it fetches logical chunk
+  // (l % 4) ^ swz(row). Rows past the matrix edge repeat the last row.
+  const char *wpanel = static_cast<const char *>(a.w) + (int64_t)n0 * a.K * 2;
+  const char *xpanel = static_cast<const char *>(a.x) + (int64_t)t0 * a.K * 2;
+  uint32_t woff[4], xoff[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = lrow + 32 * j;
-    woff[j] = (int64_t)min(n0 + row, a.N - 1) * a.K + lchunk * 8;
-    xoff[j] = (int64_t)min(t0 + row, a.M - 1) * a.K + lchunk * 8;
-    soff[j] = row * BK + swz(row, lchunk) * 8;
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 4 + j) * 16 + (lane >> 2);
+    const int lc = swz(row, lane & 3);
+    woff[j] = (uint32_t)(min(n0 + row, a.N - 1) - n0) * (uint32_t)a.K * 2u + lc * 16u;
+    xoff[j] = (uint32_t)(min(t0 + row, a.M - 1) - t0) * (uint32_t)a.K * 2u + lc * 16u;
   }
-
-  u32x4 wreg[8], xreg[8];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      wreg[j] = *reinterpret_cast<const u32x4 *>(wsrc + woff[j] + k0);
-      xreg[j] = *reinterpret_cast<const u32x4 *>(xsrc + xoff[j] + k0);
-    }
-  };
-  auto sstore = [&](int stage) {
-    bf16 *sw = lds + stage * 2 * TILE_ELEMS;
+  auto dload = [&](int stage, int k0) {
+    const char *wp = wpanel + (int64_t)k0 * 2;
+    const char *xp = xpanel + (int64_t)k0 * 2;
+    bf16 *sw = lds + stage * 2 * TILE_ELEMS + wave * 4 * 512;
     bf16 *sx = sw + TILE_ELEMS;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      *reinterpret_cast<u32x4 *>(sw + soff[j]) = wreg[j];
-      *reinterpret_cast<u32x4 *>(sx + soff[j]) = xreg[j];
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_global_load_lds(wp + woff[j], (lds_void *)(sw + j * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(xp + xoff[j], (lds_void *)(sx + j * 512), 16, 0, 0);
     }
   };
+
+  // fragment reads: lane row r32 of each 32-row block, k chunk 2 s + kh of the K
+  // tile (k-step s of 16); the swizzle depends on r32 only, so block b sits at a
+  // fixed offset of b * 32 rows
+  const int r32 = lane & 31, kh = lane >> 5;
+  int fa_base[2], fb_base[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    fa_base[s] = (wn * 128 + r32) * BK + (swz(r32, 2 * s + kh) * 8);
+    fb_base[s] = (wt * 128 + r32) * BK + (swz(r32, 2 * s + kh) * 8);
+  }
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -185,44 +201,108 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // fragment read offsets (rows of this wave, lane's row within a 32-block)
-  const int c = lane & 31, G = lane >> 5;
-  int arow[4], brow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    arow[i] = wn * 128 + i * 32 + c;
-    brow[i] = wt * 128 + i * 32 + c;
-  }
-
   const int ktiles = a.K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
 
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ktiles) gload((kt + 1) * BK);
-    const bf16 *sw = lds + cur * 2 * TILE_ELEMS;
+  // Fragments are double buffered; the next k-step's are all requested during
+  // the first half of the current one, so the wait before the next k-step is
+  // free.
+  bf16x8 fa[2][4], fb[2][4];
+  auto fload_all = [&](int stage, int s, int buf) {
+    const bf16 *sw = lds + stage * 2 * TILE_ELEMS;
     const bf16 *sx = sw + TILE_ELEMS;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int ch = 2 * s + G;
-      bf16x8 af[4], bfr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        af[i] = *reinterpret_cast<const bf16x8 *>(sw + arow[i] * BK + swz(arow[i], ch) * 8);
-        bfr[i] = *reinterpret_cast<const bf16x8 *>(sx + brow[i] * BK + swz(brow[i], ch) * 8);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    for (int i = 0; i < 4; ++i) {
+      fb[buf][i] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[s] + i * 32 * BK);
+      fa[buf][i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[s] + i * 32 * BK);
     }
-    if (kt + 1 < ktiles) sstore(cur ^ 1);
-    __syncthreads();
-  }
+  };
+  // One k-step of 16 MFMAs on buffer BCUR. When NEXT, the fragments of the next
+  // k-step (LDS stage nstage, k-step ns) are fetched into the other buffer.
+  // When SYNC >= 0, the wave first waits (after the first 4 MFMAs) until at most
+  // SYNC of its tile loads are in flight and meets the other waves, so that
+  // the next tile is in LDS for everyone; with REFILL it then starts loading
+  // tile kt + NSTAGE - 1 into the stage that tile kt - 1 used.
+  auto kstep = [&](auto bcur_c, auto next_c, auto sync_c, auto refill_c, int nstage, int ns,
+                   int kt) {
+    constexpr int BCUR = decltype(bcur_c)::value, SYNC = decltype(sync_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value, REFILL = decltype(refill_c)::value;
+    const bf16 *sw = lds + nstage * 2 * TILE_ELEMS;
+    const bf16 *sx = sw + TILE_ELEMS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[BCUR][i], fb[BCUR][j], acc[i][j]);
+      if constexpr (SYNC >= 0) {
+        if (i == 0) {
+          tile_barrier<SYNC>();
+          if constexpr (REFILL) dload((kt + NSTAGE - 1) & (NSTAGE - 1), (kt + NSTAGE - 1) * BK);
+        }
+      }
+      if constexpr (NEXT) {
+        if (i < 2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (i == 0)
+              fb[BCUR ^ 1][r] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + r * 32 * BK);
+            else
+              fa[BCUR ^ 1][r] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + r * 32 * BK);
+          }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMA
+        if (i < 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using S0 = std::integral_constant<int, 0>;
+  using S8 = std::integral_constant<int, 8>;
+  using NOSYNC = std::integral_constant<int, -1>;
+  using Y = std::true_type;
+  using N = std::false_type;
+  const int stage_mask = NSTAGE - 1;
 
-  epilogue<EPI>(a, acc, n0 + wn * 128, t0 + wt * 128, lane);
+  // Pipeline: NSTAGE - 1 tiles in flight. Tile kt's second k-step waits (once)
+  // for tile kt+1 to land, then refills the stage of tile kt-1 with tile
+  // kt+NSTAGE-1 and reads tile kt+1's first fragments while it multiplies.
+  // The last tiles are peeled so that every wait count is a constant.
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p)
+    if (p < ktiles) dload(p, p * BK);
+  if (ktiles >= 3) tile_barrier<16>();
+  else if (ktiles == 2) tile_barrier<8>();
+  else tile_barrier<0>();
+  fload_all(0, 0, 0);
+  // settle every counter once (including scalar loads, which would otherwise
+  // make the compiler wait for all LDS reads at each k-step)
+  __builtin_amdgcn_s_waitcnt(0);
+  int kt = 0;
+  for (; kt + 3 < ktiles; ++kt) {
+    kstep(I0(), Y(), NOSYNC(), N(), kt & stage_mask, 1, kt);
+    kstep(I1(), Y(), S8(), Y(), (kt + 1) & stage_mask, 0, kt);
+  }
+  if (kt + 2 < ktiles) {  // tile kt+2 still in flight behind kt+1
+    kstep(I0(), Y(), NOSYNC(), N(), kt & stage_mask, 1, kt);
+    kstep(I1(), Y(), S8(), N(), (kt + 1) & stage_mask, 0, kt);
+    ++kt;
+  }
+  if (kt + 1 < ktiles) {  // only tile kt+1 in flight
+    kstep(I0(), Y(), NOSYNC(), N(), kt & stage_mask, 1, kt);
+    kstep(I1(), Y(), S0(), N(), (kt + 1) & stage_mask, 0, kt);
+    ++kt;
+  }
+  kstep(I0(), Y(), NOSYNC(), N(), kt & stage_mask, 1, kt);
+  kstep(I1(), N(), NOSYNC(), N(), 0, 0, kt);
+
+  const int nb = n0 + wn * 128 + 4 * kh, tb = t0 + wt * 128 + r32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<EPI>(a, tb + 32 * j, nb + 32 * i + 8 * g, acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                    acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
 }
 
 }  // namespace
