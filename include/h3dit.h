@@ -136,8 +136,10 @@ int h3dit_rope_table(const h3dit_config *cfg, const int32_t *positions, float *t
 /* Steps 3 + 4, QKV projection with RoPE in the epilogue:
  *   h [T, D] bf16, w_qkv [3A, D] bf16, table from h3dit_rope_table.
  *   qk [T, 2A] bf16: columns 0..A-1 = bf16(rope(bf16(q))), A..2A-1 = same for k.
- *   vt [H, 128, Tp] bf16 with Tp = h3dit_padded_tokens(T): v transposed per head,
- *      columns T..Tp-1 written as zero. */
+ *   vt [H, 128, Tp] bf16 with Tp = h3dit_padded_tokens(T): v transposed per head;
+ *      the value of token t sits in column t with bits 2 and 3 of t exchanged
+ *      (the order in which the attention kernel's matrix-core fragments take
+ *      keys); columns of tokens T..Tp-1 are written as zero. */
 int h3dit_qkv_rope(const h3dit_config *cfg, const void *h, const void *w_qkv, const float *table,
                    void *qk, void *vt, void *stream);
 

@@ -90,7 +90,9 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
     } else {
       if (t >= a.Mp) return;
       const int hv = n - A2;  // head * 128 + dim
-      bf16 *vt = static_cast<bf16 *>(a.out2) + (int64_t)hv * a.Mp + t;
+      // token t is stored at column t with bits 2 and 3 exchanged (see attention)
+      const int col = (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+      bf16 *vt = static_cast<bf16 *>(a.out2) + (int64_t)hv * a.Mp + col;
       const bool live = t < a.M;
       vt[0] = to_bf16(live ? v0 : 0.0f);
       vt[a.Mp] = to_bf16(live ? v1 : 0.0f);

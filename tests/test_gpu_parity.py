@@ -43,6 +43,13 @@ def f64_dev(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).cuda()
 
 
+def unswap_vt(vt):
+    """vt columns hold token t at t with bits 2 and 3 exchanged; undo that."""
+    cols = np.arange(vt.shape[-1])
+    src = (cols & ~12) | ((cols & 4) << 1) | ((cols & 8) >> 1)
+    return vt[..., src]
+
+
 def host(t):
     torch.cuda.synchronize()
     return t.detach().cpu().to(torch.float64).numpy()
@@ -115,7 +122,7 @@ def test_stage_qkv_rope(cfg):
     k = O.bf16_round(O.apply_rope(O.bf16_round(h1 @ wk.T).reshape(T, H, 128), pos, cfg.rope_base))
     v = O.bf16_round(h1 @ wv.T).reshape(T, H, 128)
     g_qk = host(qk)
-    g_vt = host(vt)
+    g_vt = unswap_vt(host(vt))
     for name, got, ref in (("q", g_qk[:, :A], q.reshape(T, A)), ("k", g_qk[:, A:], k.reshape(T, A)),
                            ("v", g_vt[:, :, :T].transpose(2, 0, 1).reshape(T, A), v.reshape(T, A))):
         # a one-ulp difference in a bf16 input of the rotation can cancel into
@@ -140,7 +147,7 @@ def test_stage_attention(cfg):
     T, A, H = cfg.n_tokens, cfg.attn_width, cfg.heads
     o = torch.empty(T, A, dtype=torch.bfloat16, device="cuda")
     B.h3dit_attention(B.config_from(cfg), qk, vt, o)
-    g_qk, g_vt = host(qk), host(vt)
+    g_qk, g_vt = host(qk), unswap_vt(host(vt))
     q = g_qk[:, :A].reshape(T, H, 128)
     k = g_qk[:, A:].reshape(T, H, 128)
     v = g_vt[:, :, :T].transpose(2, 0, 1)
