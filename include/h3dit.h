@@ -21,8 +21,10 @@
  * Precision: weights and matrix-core operands are bf16 (round to nearest
  * even); products accumulate in fp32; the modulation vector and both
  * normalisations are computed in fp64; x1 and the output are fp32. The
- * attention weights are bf16(2^(s - ceil(running max of s))) with
- * s = q.k * log2(e)/sqrt(128), normalised by their own sum.
+ * stored query carries the softmax factor: q = bf16(rope(q) * log2(e)/sqrt(128)),
+ * rounded once, so a score s = q.k is a base-2 exponent; the attention
+ * weights are bf16(2^(s - m)) for an integer shift m per query (the rounded-up
+ * maximum score), normalised by their own sum.
  *
  * Memory: every pointer argument is a DEVICE pointer unless marked (host);
  * matrices are row-major and dense; the caller owns all memory, including the
@@ -135,7 +137,9 @@ int h3dit_rope_table(const h3dit_config *cfg, const int32_t *positions, float *t
 
 /* Steps 3 + 4, QKV projection with RoPE in the epilogue:
  *   h [T, D] bf16, w_qkv [3A, D] bf16, table from h3dit_rope_table.
- *   qk [T, 2A] bf16: columns 0..A-1 = bf16(rope(bf16(q))), A..2A-1 = same for k.
+ *   qk [T, 2A] bf16: columns 0..A-1 = bf16(rope(q) * log2(e)/sqrt(128)),
+ *      columns A..2A-1 = bf16(rope(k)); q and k are the fp32 products, rounded
+ *      once after the rotation.
  *   vt [H, 128, Tp] bf16 with Tp = h3dit_padded_tokens(T): v transposed per head;
  *      the value of token t sits in column t with bits 2 and 3 of t exchanged
  *      (the order in which the attention kernel's matrix-core fragments take
@@ -144,7 +148,8 @@ int h3dit_qkv_rope(const h3dit_config *cfg, const void *h, const void *w_qkv, co
                    void *qk, void *vt, void *stream);
 
 /* Step 5, joint bidirectional attention over all T tokens (no mask):
- *   qk, vt as written by h3dit_qkv_rope; o [T, A] bf16 (head h = columns h*128..). */
+ *   qk, vt as written by h3dit_qkv_rope (q pre-scaled, so softmax(q.k) in base 2);
+ *   o [T, A] bf16 (head h = columns h*128..). */
 int h3dit_attention(const h3dit_config *cfg, const void *qk, const void *vt, void *o,
                     void *stream);
 

@@ -5,26 +5,38 @@
 // with an online softmax, so no T x T matrix is ever stored.
 //
 // Work split: a workgroup owns 256 queries of one head (eight waves of 32, two
-// waves per SIMD so that one wave's softmax overlaps the other's matrix-core
-// work). Each wave computes the transposed score tile S^T = K Q^T with the
-// 32x32x16 bf16 MFMA, so a lane holds 32 of the 64 scores of ONE query (the
-// other 32 sit in lane l ^ 32): row maxima and sums need one cross-lane
-// exchange. The output is accumulated transposed as well, O^T += V^T P^T;
-// the MFMA's K slots of that product are assigned to keys in the order in
-// which the score registers hold them (lane half G holds keys 4G..4G+3 and
-// 8+4G..8+4G+3 of every 16), and V^T is stored in global memory with bits 2
-// and 3 of the key index exchanged, so each such fragment is one 16-byte read.
+// waves per SIMD). Each wave computes the transposed score tile S^T = K Q^T
+// with the 32x32x16 bf16 MFMA, so a lane holds 32 of the 64 scores of ONE
+// query (the other 32 sit in lane l ^ 32). The output is accumulated
+// transposed as well, O^T += V^T P^T; the MFMA's K slots of that product are
+// assigned to keys in the order in which the score registers hold them (lane
+// half G holds keys 4G..4G+3 and 8+4G..8+4G+3 of every 16), and V^T is stored
+// in global memory with bits 2 and 3 of the key index exchanged, so each such
+// fragment is one 16-byte read.
 //
-// Softmax weights: s = q.k * log2(e) / sqrt(128); the running maximum is
-// rounded up to an integer m, and P = bf16(2^(s - m)). Because rescaling
-// between tiles is by an exact power of two, the bf16 weights do not depend
-// on the order of the key tiles; o = bf16(sum P v / sum P), where the sum
-// runs over the rounded weights.
+// Pipeline: after the barrier of key tile i, a wave multiplies the scores of
+// tile i+1 on the matrix cores while its vector ALUs turn the scores of tile i
+// into weights, then accumulates P(i) V(i). K and V^T tiles are double
+// buffered in LDS and stream in one tile ahead through gfx950's global-to-LDS
+// loads; there is one barrier per tile.
 //
-// K tiles ([64 keys][128 dims], 256-byte rows, 16-byte chunk c stored at
-// c ^ (row & 15)) and V^T tiles ([128 dims][64 keys], 128-byte rows, chunk c at
-// c ^ ((row >> 1) & 7)) stream straight from global memory into a 3-stage LDS
-// ring (gfx950's global-load-to-LDS), two tiles ahead, one barrier per tile.
+// Softmax weights. The stored queries already carry the factor log2(e)/sqrt(128)
+// (the QKV epilogue applies it before rounding q to bf16), so a score
+// s = q.k is in base-2 units, and P = bf16(2^(s - m)) for an integer shift m
+// per query. The score MFMAs start their accumulation from -m, so the matrix
+// cores deliver s - m and each weight costs one exp2. m is not raised tile by
+// tile: it is set from the first tile's maximum, and afterwards only when
+// some lane's sum of its 32 new weights exceeds 2^32 is the tile's maximum
+// taken, m raised to its rounded-up value, the running output and sum
+// rescaled by the exact power of two 2^(m_old - m_new), and the tile's weights
+// formed again. Every weight is therefore at most 2^32. Because rescaling by
+// a power of two commutes with bf16 rounding, the result equals that of the
+// single shift ceil(max over all keys): o = bf16(sum P v / sum P), the sum
+// taken over the rounded weights.
+//
+// LDS layouts: K tile [64 keys][128 dims], 256-byte rows, 16-byte chunk c
+// stored at c ^ (row & 15); V^T tile [128 dims][64 keys], 128-byte rows,
+// chunk c at c ^ ((row >> 1) & 7). Both make the fragment reads conflict-free.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,42 +50,51 @@ constexpr int NW = 8;              // waves per workgroup
 constexpr int QT = 32 * NW;        // queries per workgroup
 constexpr int NTHREADS = 64 * NW;  // threads per workgroup
 constexpr int KT = 64;             // keys per tile
-constexpr int NST = 3;             // LDS stages
 constexpr int K_ELEMS = KT * 128;  // bf16 elements of one K tile (16 KB)
 constexpr int V_ELEMS = 128 * KT;  // bf16 elements of one V^T tile (16 KB)
-constexpr int STAGE_ELEMS = K_ELEMS + V_ELEMS;
+constexpr int KSTAGE0 = 0, VSTAGE0 = 2 * K_ELEMS;  // [K0 | K1 | V0 | V1], 64 KB
+// A lane's weight sum per tile that forces a new shift. Weights up to 2^32
+// keep every fp32 sum (at most 2^20 keys) far below overflow.
+constexpr float SUM_LIMIT = 4294967296.0f;
 
-typedef __attribute__((address_space(3))) void lds_void;
+// One 16-byte global -> LDS copy per lane: lane l reads base + voff (bytes) and
+// writes LDS bytes lds_addr + 16 l. Issued as an instruction the compiler does
+// not model, so that it keeps counting LDS reads precisely (with such a copy in
+// flight it otherwise waits for every LDS read at each use); completion is
+// awaited explicitly by tile_barrier.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(base), "s"(lds_addr)
+               : "memory");
+}
 
-// Wait until at most N of this wave's tile loads are in flight (they complete
-// in issue order), then meet the other waves.
-template <int N>
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+
+// Wait for all of this wave's tile copies, then meet the other waves.
 __device__ __forceinline__ void tile_barrier() {
-  constexpr int enc = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  constexpr int enc = (0x7 << 4) | (0xF << 8);  // vmcnt(0)
   __builtin_amdgcn_s_waitcnt(enc);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
-  u32x4 u = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
-             __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
-  return __builtin_bit_cast(bf16x8, u);
-}
-
 __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__restrict__ qk,
-                                                          const bf16 *__restrict__ vt,
-                                                          bf16 *__restrict__ o, int T, int H,
-                                                          int Tp) {
-  __shared__ __attribute__((aligned(1024))) bf16 lds[NST * STAGE_ELEMS];  // 96 KB
+                                                                const bf16 *__restrict__ vt,
+                                                                bf16 *__restrict__ o, int T,
+                                                                int H, int Tp) {
+  __shared__ __attribute__((aligned(1024))) bf16 lds[2 * K_ELEMS + 2 * V_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 5, c = lane & 31;
   const int h = blockIdx.y;
   const int A = H * 128;
-  const int64_t ldqk = 2 * (int64_t)A;
+  const int ldqk = 2 * A;
   const int q0 = blockIdx.x * QT + wave * 32;
+  const int ntiles = (int)ceil_div(T, KT);
 
   // this lane's query fragments: Q[q0 + c][16 s + 8 G .. +7], s = 0..7
   bf16x8 qf[8];
@@ -84,139 +105,217 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
     for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
   }
 
-  // Tile loads: wave w fills 1 KB blocks 2w, 2w+1 of the K tile (4 rows of 256 B
-  // each) and of the V^T tile (8 rows of 128 B each). Lane l lands at byte 16 l
+  // Tile copies: wave w fills 1 KB blocks 2w, 2w+1 of a K tile (4 rows of 256 B
+  // each) and of a V^T tile (8 rows of 128 B each). Lane l lands at byte 16 l
   // of its block, so it fetches the logical chunk that the swizzle puts there.
-  const bf16 *ksrc[2];
-  const bf16 *vsrc[2];
-  int krow[2];
+  // Byte offsets are relative to the tile's first row (K) or the head's first
+  // dim row and the tile's first key (V^T).
+  const bf16 *khead = qk + A + h * 128;
+  const bf16 *vhead = vt + (int64_t)h * 128 * Tp;
+  int krow[2], kcol[2];
+  uint32_t kofs[2], vofs[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int kr = (2 * wave + j) * 4 + (lane >> 4);  // key row within the tile
-    const int kc = (lane & 15) ^ (kr & 15);
     krow[j] = kr;
-    ksrc[j] = qk + A + h * 128 + kc * 8;
+    kcol[j] = ((lane & 15) ^ (kr & 15)) * 8;
+    kofs[j] = (uint32_t)(kr * ldqk + kcol[j]) * 2u;
     const int vr = (2 * wave + j) * 8 + (lane >> 3);  // dim row of V^T
-    const int vc = (lane & 7) ^ ((vr >> 1) & 7);
-    vsrc[j] = vt + (int64_t)(h * 128 + vr) * Tp + vc * 8;
+    vofs[j] = (uint32_t)(vr * Tp + ((lane & 7) ^ ((vr >> 1) & 7)) * 8) * 2u;
   }
-  auto tload = [&](int stage, int kv0) {
-    bf16 *sk = lds + stage * STAGE_ELEMS + wave * 2 * 512;
-    bf16 *sv = lds + stage * STAGE_ELEMS + K_ELEMS + wave * 2 * 512;
+  const uint32_t lds0 = lds_address(lds);
+  auto kload = [&](int stage, int tile) {
+    const uint32_t dst = lds0 + (uint32_t)(KSTAGE0 + stage * K_ELEMS + wave * 2 * 512) * 2u;
+    const bf16 *base = khead + (int64_t)tile * KT * ldqk;
+    const int rows = T - tile * KT;  // keys present in this tile
+    if (rows >= KT) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key = min(kv0 + krow[j], T - 1);
-      __builtin_amdgcn_global_load_lds(ksrc[j] + (int64_t)key * ldqk, (lds_void *)(sk + j * 512),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc[j] + kv0, (lds_void *)(sv + j * 512), 16, 0, 0);
+      for (int j = 0; j < 2; ++j) dma16(base, kofs[j], dst + j * 1024);
+    } else {  // ragged last tile: rows past T repeat row T - 1
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        dma16(base, (uint32_t)(min(krow[j], rows - 1) * ldqk + kcol[j]) * 2u, dst + j * 1024);
     }
   };
+  auto vload = [&](int stage, int tile) {
+    const uint32_t dst = lds0 + (uint32_t)(VSTAGE0 + stage * V_ELEMS + wave * 2 * 512) * 2u;
+    const bf16 *base = vhead + tile * KT;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(base, vofs[j], dst + j * 1024);
+  };
 
-  // fragment read offsets within a stage (elements)
-  int koff[2][8];
+  // Fragment read offsets (elements) within stage 0. The swizzles depend only
+  // on the lane's row within a 16-row (K) or 32-row (V^T) group, so the other
+  // key block, the other dim blocks and the other stage are immediate offsets.
+  int koff[8];  // K row c, 16-byte chunk 2 s + G
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int s = 0; s < 8; ++s) koff[s] = KSTAGE0 + c * 128 + (((2 * s + G) ^ (c & 15)) * 8);
+  int voff[4];  // V^T row c, 16-byte chunk 2 j + G
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int r = 32 * b + c;
-      koff[b][s] = r * 128 + (((2 * s + G) ^ (r & 15)) * 8);
-    }
-  int voff[4][4];  // [db][chunk pair index p = 2 b + half]
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int d = db * 32 + c;
-      voff[db][p] = K_ELEMS + d * 64 + (((2 * p + G) ^ ((d >> 1) & 7)) * 8);
-    }
+  for (int j = 0; j < 4; ++j) voff[j] = VSTAGE0 + c * 64 + (((2 * j + G) ^ ((c >> 1) & 7)) * 8);
 
   f32x16 oacc[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[d][v] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = 0.0f, l_run = 0.0f;
+  f32x16 negm;  // -m_run in every element: the score MFMAs start from it
+#pragma unroll
+  for (int v = 0; v < 16; ++v) negm[v] = 0.0f;
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  f32x16 sacc[2][2];  // [parity][key block]: s - m of one tile
+  u32x4 pf[4];        // P^T fragments of the four k-steps of P V
 
-  const int ntiles = (int)ceil_div(T, KT);
-  tload(0, 0);
-  if (ntiles > 1) tload(1, KT);
+  // S^T(tile) - m from K stage KS into sacc[KS]
+  auto scores = [&](auto ks_c) {
+    constexpr int KS = decltype(ks_c)::value;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8 *>(lds + koff[s] + b * 32 * 128 + KS * K_ELEMS);
+        sacc[KS][b] = mfma32(kf, qf[s], s == 0 ? negm : sacc[KS][b]);
+      }
+  };
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int stage = it % NST;
-    const int kv0 = it * KT;
-    // tile it has landed for every wave, and tile it-1's stage is free
-    if (it + 1 < ntiles) tile_barrier<4>();
-    else tile_barrier<0>();
-    if (it + 2 < ntiles) tload((it + 2) % NST, (it + 2) * KT);
-    const bf16 *sb = lds + stage * STAGE_ELEMS;
-
-    // S^T[key][query] for keys kv0 + 32 b + (8 (v/4) + 4 G + v%4), query q0 + c
-    f32x16 sacc[2];
+  // P = bf16(2^(sacc - dm)) straight into the P^T fragments (fragment j holds
+  // registers 8 (j % 2) .. +7 of score block j / 2); returns this lane's sum
+  // of its 32 weights.
+  auto weights = [&](auto p_c, float dm) -> float {
+    constexpr int P = decltype(p_c)::value;
+    float t[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[b][v] = 0.0f;
+      for (int u = 0; u < 8; ++u) {
+        const float p0 = __builtin_amdgcn_exp2f(sacc[P][b][2 * u] - dm);
+        const float p1 = __builtin_amdgcn_exp2f(sacc[P][b][2 * u + 1] - dm);
+        const bf16x2 pr = pack2(p0, p1);
+        pf[2 * b + (u >> 2)][u & 3] = __builtin_bit_cast(uint32_t, pr);
+        t[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, t[u & 1], false);
+      }
+    return t[0] + t[1];
+  };
+
+  // O^T[dim][query] += V^T[dim][keys] P^T[keys][query] from V stage VS
+  auto pv = [&](auto vs_c) {
+    constexpr int VS = decltype(vs_c)::value;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 pj = __builtin_bit_cast(bf16x8, pf[j]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(sb + koff[b][s]);
-        sacc[b] = mfma32(kf, qf[s], sacc[b]);
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 vf =
+            *reinterpret_cast<const bf16x8 *>(lds + voff[j] + VS * V_ELEMS + db * 32 * 64);
+        oacc[db] = mfma32(vf, pj, oacc[db]);
       }
     }
+    // fragment reads run four MFMAs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int k = 0; k < 12; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  };
 
+  // One tile: copies of K(it + 2) and V(it + 1), S(it + 1) (when NEXT_S)
+  // overlapped with the weights of tile it, the shift check, then P V.
+  auto step = [&](auto p_c, auto next_s_c, int it) {
+    constexpr int P = decltype(p_c)::value;
+    constexpr bool NEXT_S = decltype(next_s_c)::value;
+    using KN = std::integral_constant<int, P ^ 1>;
+    tile_barrier();  // V(it) and K(it + 1) are in LDS everywhere
+    if (it + 2 < ntiles) kload(P, it + 2);
+    if (it + 1 < ntiles) vload(P ^ 1, it + 1);
+
+    const int kv0 = it * KT;
     if (kv0 + KT > T) {  // ragged last tile: keys past T get zero weight
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kv0 + 32 * b + 8 * (v >> 2) + 4 * G + (v & 3);
-          if (key >= T) sacc[b][v] = -INFINITY;
+          if (key >= T) sacc[P][b][v] = -INFINITY;
         }
     }
 
-    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+    if constexpr (NEXT_S) scores(KN());
+    float ts = weights(p_c, 0.0f);
+    if constexpr (NEXT_S) {
+      // score MFMAs interleaved with the weight computation, K fragment reads
+      // running four MFMAs ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(sacc[0][v], sacc[1][v]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, ceilf(mx * kLog2eOverSqrt128));
-    if (__ballot(m_new > m_run)) {
-      const float f = __builtin_amdgcn_exp2f(m_run - m_new);  // exact power of two (0 at start)
-      l_run *= f;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[d][v] *= f;
-    }
-    m_run = m_new;
-
-    // P = bf16(2^(s - m)), packed in pairs; row sum over the rounded weights
-    bf16x2 pk[2][8];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[b][2 * u], kLog2eOverSqrt128, -m_new));
-        const float p1 =
-            __builtin_amdgcn_exp2f(fmaf(sacc[b][2 * u + 1], kLog2eOverSqrt128, -m_new));
-        pk[b][u] = pack2(p0, p1);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pk[b][u], ones, l_run, false);
+      for (int k = 0; k < 12; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-
-    // O^T[dim][query] += V^T[dim][keys] P^T[keys][query]; K step j covers
-    // score block b = j / 2, registers 8 (j % 2) .. +7.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int b = j >> 1, half = j & 1;
-      const bf16x8 pf = as_bf16x8(pk[b][4 * half], pk[b][4 * half + 1], pk[b][4 * half + 2],
-                                  pk[b][4 * half + 3]);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(sb + voff[db][j]);
-        oacc[db] = mfma32(vf, pf, oacc[db]);
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
     }
+
+    // First tile: take the shift from its maximum. Later tiles: only when the
+    // weights grew past 2^32 (or overflowed).
+    if (__ballot((ts > SUM_LIMIT) | (it == 0))) {
+      float mx = fmaxf(sacc[P][0][0], sacc[P][1][0]);
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(sacc[P][0][v], sacc[P][1][v]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float dm = ceilf(mx);  // integer step of the shift
+      if (it > 0) {
+        dm = fmaxf(dm, 0.0f);
+        const float fct = __builtin_amdgcn_exp2f(-dm);  // exact power of two
+        l_run *= fct;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[d][v] *= fct;
+      }
+      m_run += dm;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) negm[v] = -m_run;
+      if constexpr (NEXT_S) {  // the next tile's scores were taken with the old shift
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sacc[P ^ 1][b][v] -= dm;
+      }
+      ts = weights(p_c, dm);
+    }
+    l_run += ts;
+    pv(p_c);
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using Y = std::true_type;
+  using N = std::false_type;
+
+  // prologue: K(0), K(1), V(0) in flight; S(0) once they land
+  kload(0, 0);
+  if (ntiles > 1) kload(1, 1);
+  vload(0, 0);
+  tile_barrier();
+  scores(I0());
+
+  int it = 0;
+  for (; it + 2 < ntiles; it += 2) {
+    step(I0(), Y(), it);
+    step(I1(), Y(), it + 1);
+  }
+  if (ntiles - it == 2) {
+    step(I0(), Y(), it);
+    step(I1(), N(), it + 1);
+  } else {
+    step(I0(), N(), it);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -76,16 +76,18 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
     const int A2 = 2 * a.A;
     if (n < A2) {
       if (t >= a.M) return;
-      // q or k: round, rotate the two adjacent pairs, round again
-      const float u0 = bf16_round_f32(v0), w0 = bf16_round_f32(v1);
-      const float u1 = bf16_round_f32(v2), w1 = bf16_round_f32(v3);
+      // q or k: rotate the two adjacent pairs of the fp32 products, then round
+      // once; q also takes the softmax factor log2(e)/sqrt(128) before its
+      // rounding, so that attention scores leave the matrix cores in base-2 units
+      const float u0 = v0, w0 = v1, u1 = v2, w1 = v3;
       const int p = (n & 127) >> 1;  // pair index within the head (0..63)
       const f32x4 cs = *reinterpret_cast<const f32x4 *>(a.table + ((int64_t)t * 64 + p) * 2);
+      const float sc = n < a.A ? kLog2eOverSqrt128 : 1.0f;
       bf16x4 r;
-      r[0] = to_bf16(u0 * cs[0] - w0 * cs[1]);
-      r[1] = to_bf16(u0 * cs[1] + w0 * cs[0]);
-      r[2] = to_bf16(u1 * cs[2] - w1 * cs[3]);
-      r[3] = to_bf16(u1 * cs[3] + w1 * cs[2]);
+      r[0] = to_bf16((u0 * cs[0] - w0 * cs[1]) * sc);
+      r[1] = to_bf16((u0 * cs[1] + w0 * cs[0]) * sc);
+      r[2] = to_bf16((u1 * cs[2] - w1 * cs[3]) * sc);
+      r[3] = to_bf16((u1 * cs[3] + w1 * cs[2]) * sc);
       *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * A2 + n) = r;
     } else {
       if (t >= a.Mp) return;

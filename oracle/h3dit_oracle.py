@@ -28,13 +28,16 @@ FFN 14336) and these readings of what the pages leave open:
 Two modes:
   * ``"exact"``: every value is float64; softmax is the plain softmax.
   * ``"contract"``: the same math, but values are rounded to bf16 exactly
-    where the GPU path stores a bf16 matrix-core operand (h1, q, k, v, the
+    where the GPU path stores a bf16 matrix-core operand (h1, v, the
     rotated q and k, the unnormalised attention weights, the attention
-    output o, h2 and the GELU output u). The attention weights are taken as
-    P = bf16(2 ** (s - ceil(max_j s))) with s = q.k * log2(e) / sqrt(128),
-    normalised by the sum of the rounded P. Mathematically this equals the
-    softmax; the integer shift only makes the bf16 weights independent of
-    the order in which keys are visited, so the GPU result can be mirrored.
+    output o, h2 and the GELU output u). q and k are rounded once, after
+    the rotation; the stored q also carries the softmax scale:
+    q = bf16(rope(q) * log2(e) / sqrt(128)), so a score s = q.k is already
+    in base-2 units. The attention
+    weights are P = bf16(2 ** (s - ceil(max_j s))), normalised by the sum of
+    the rounded P. Mathematically this equals the softmax; the integer shift
+    only makes the bf16 weights independent of the order in which keys are
+    visited, so the GPU result can be mirrored.
 
 All arithmetic other than the bf16 rounding points is float64.
 Parity pins: every function here is checked in the CPU test-suite against
@@ -133,19 +136,30 @@ def apply_rope(t: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # step a5: joint bidirectional attention
 # ----------------------------------------------------------------------------
+def scaled_query(q: np.ndarray) -> np.ndarray:
+    """Contract-mode stored query: bf16(q * log2(e) / sqrt(dh)), rounded once.
+
+    Folding the softmax scale (1/sqrt(dh), and the change of base from e to 2)
+    into the query before its single bf16 rounding keeps one rounding per
+    stored element, as for k; softmax(q.k / sqrt(dh)) = 2^(q'.k) / sum 2^(q'.k).
+    """
+    return bf16_round(q * (LOG2E / math.sqrt(q.shape[-1])))
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mode: str) -> np.ndarray:
     """o[Tq, H, dh] for queries q[Tq, H, dh] against all keys k, v[Tk, H, dh].
 
     exact:    o = softmax(q k^T / sqrt(dh)) v
-    contract: s = (q k^T) * log2(e) / sqrt(dh);  P = bf16(2**(s - ceil(max s)));
-              o = bf16( (P v) / sum(P) )
+    contract: q already carries the factor log2(e) / sqrt(dh) (see
+              scaled_query), so s = q k^T is the base-2 exponent;
+              P = bf16(2**(s - ceil(max s)));  o = bf16( (P v) / sum(P) )
     """
     Tq, H, dh = q.shape
     out = np.empty((Tq, H, dh), dtype=np.float64)
     for h in range(H):
         scores = q[:, h, :] @ k[:, h, :].T                       # [Tq, Tk]
         if mode == "contract":
-            s = scores * (LOG2E / math.sqrt(dh))
+            s = scores
             m = np.ceil(np.max(s, axis=1, keepdims=True))
             p = bf16_round(np.exp2(s - m))
             out[:, h, :] = bf16_round((p @ v[:, h, :]) / np.sum(p, axis=1, keepdims=True))
@@ -194,12 +208,14 @@ def block_forward(x: np.ndarray, cond: np.ndarray, w: Dict[str, np.ndarray], pos
 
     # a3: projections; k and v over all tokens, q over the requested rows
     w_q, w_k, w_v = w["w_qkv"][:A], w["w_qkv"][A:2 * A], w["w_qkv"][2 * A:]
-    q = _round(h1[r] @ w_q.T, mode).reshape(len(r), heads, dh)
-    k = _round(h1 @ w_k.T, mode).reshape(T, heads, dh)
+    q = (h1[r] @ w_q.T).reshape(len(r), heads, dh)
+    k = (h1 @ w_k.T).reshape(T, heads, dh)
     v = _round(h1 @ w_v.T, mode).reshape(T, heads, dh)
 
-    # a4: RoPE on q and k
-    q = _round(apply_rope(q, pos[r], rope_base), mode)
+    # a4: RoPE on q and k; each is rounded to bf16 once, after the rotation
+    # (and, for q, after the softmax scale)
+    q = apply_rope(q, pos[r], rope_base)
+    q = scaled_query(q) if mode == "contract" else q
     k = _round(apply_rope(k, pos, rope_base), mode)
 
     # a5: attention of the requested queries against every key

@@ -118,8 +118,8 @@ def test_stage_qkv_rope(cfg):
     h1, w, pos, qk, vt = _qkv_stage(cfg, inp)
     T, A, H = cfg.n_tokens, cfg.attn_width, cfg.heads
     wq, wk, wv = w["w_qkv"][:A], w["w_qkv"][A:2 * A], w["w_qkv"][2 * A:]
-    q = O.bf16_round(O.apply_rope(O.bf16_round(h1 @ wq.T).reshape(T, H, 128), pos, cfg.rope_base))
-    k = O.bf16_round(O.apply_rope(O.bf16_round(h1 @ wk.T).reshape(T, H, 128), pos, cfg.rope_base))
+    q = O.scaled_query(O.apply_rope((h1 @ wq.T).reshape(T, H, 128), pos, cfg.rope_base))
+    k = O.bf16_round(O.apply_rope((h1 @ wk.T).reshape(T, H, 128), pos, cfg.rope_base))
     v = O.bf16_round(h1 @ wv.T).reshape(T, H, 128)
     g_qk = host(qk)
     g_vt = unswap_vt(host(vt))

@@ -192,14 +192,16 @@ def test_attention_bruteforce_tiny():
 
 
 def _contract_bruteforce(q, k, v):
-    """The rounded-weights form in pure Python: bf16 via _bf16_scalar."""
+    """The rounded-weights form in pure Python: bf16 via _bf16_scalar; q is the
+    raw query, scaled by log2(e)/sqrt(dh) and rounded here element by element."""
     Tq, H, dh = q.shape
     Tk = k.shape[0]
     c = math.log2(math.e) / math.sqrt(dh)
     out = np.zeros((Tq, H, dh))
     for h in range(H):
         for i in range(Tq):
-            s = [sum(q[i, h, d] * k[j, h, d] for d in range(dh)) * c for j in range(Tk)]
+            qs = [_bf16_scalar(float(q[i, h, d]) * c) for d in range(dh)]
+            s = [sum(qs[d] * k[j, h, d] for d in range(dh)) for j in range(Tk)]
             m = math.ceil(max(s))
             p = [_bf16_scalar(2.0 ** (x - m)) for x in s]
             z = sum(p)
@@ -212,7 +214,7 @@ def test_attention_contract_bruteforce_tiny():
     q = O.bf16_round(RNG.standard_normal((4, 2, 8)) * 3)
     k = O.bf16_round(RNG.standard_normal((9, 2, 8)) * 3)
     v = O.bf16_round(RNG.standard_normal((9, 2, 8)))
-    got = O.attention(q, k, v, "contract")
+    got = O.attention(O.scaled_query(q), k, v, "contract")
     ref = _contract_bruteforce(q, k, v)
     # the sums may differ in the last float64 bit, which can flip a bf16 rounding
     # of o only at an exact tie; require near-equality and mostly exact equality
@@ -257,14 +259,30 @@ def test_attention_special_cases(mode):
         np.testing.assert_allclose(a, b, rtol=2 ** -7, atol=1e-12)
 
 
+def test_scaled_query_rounds_once():
+    q = RNG.standard_normal((3, 2, 128)) * 4
+    c = math.log2(math.e) / math.sqrt(128)
+    ref = np.vectorize(lambda x: _bf16_scalar(x * c))(q)
+    np.testing.assert_array_equal(O.scaled_query(q), ref)
+    # the change of base: 2^(c x) = e^(x / sqrt(128)) for the unrounded product
+    x = np.linspace(-30, 30, 7)
+    np.testing.assert_allclose(np.exp2(c * x), np.exp(x / math.sqrt(128)), rtol=1e-14)
+
+
 def test_attention_contract_close_to_exact():
     q = O.bf16_round(RNG.standard_normal((64, 2, 128)))
     k = O.bf16_round(RNG.standard_normal((200, 2, 128)))
     v = O.bf16_round(RNG.standard_normal((200, 2, 128)))
     a = O.attention(q, k, v, "exact")
-    b = O.attention(q, k, v, "contract")
-    # rounded weights carry relative error <= 2**-9 each; o is rounded once more
-    bound = 2 ** -9 * 2 * np.abs(v).max() + 2 ** -9 * np.abs(a)
+    qs = O.scaled_query(q)
+    b = O.attention(qs, k, v, "contract")
+    # Rounding the scaled query (relative 2**-9 per element) moves each base-2
+    # score by at most ds = 2**-9 sum_d |q's k|; each rounded weight then
+    # carries relative error <= 2**ds - 1 + 2**-9, which moves the normalised
+    # output by at most twice that times max |v|; o is rounded once more.
+    ds = 2 ** -9 * np.einsum("ihd,jhd->ihj", np.abs(qs), np.abs(k)).max(axis=2)  # [Tq, H]
+    eps = (2 ** ds - 1 + 2 ** -9)[..., None]
+    bound = 2 * eps * np.abs(v).max() + 2 ** -9 * np.abs(a)
     assert np.all(np.abs(a - b) <= bound + 1e-12)
 
 
