@@ -57,22 +57,6 @@ constexpr int KSTAGE0 = 0, VSTAGE0 = 2 * K_ELEMS;  // [K0 | K1 | V0 | V1], 64 KB
 // keep every fp32 sum (at most 2^20 keys) far below overflow.
 constexpr float SUM_LIMIT = 4294967296.0f;
 
-// One 16-byte global -> LDS copy per lane: lane l reads base + voff (bytes) and
-// writes LDS bytes lds_addr + 16 l. Issued as an instruction the compiler does
-// not model, so that it keeps counting LDS reads precisely (with such a copy in
-// flight it otherwise waits for every LDS read at each use); completion is
-// awaited explicitly by tile_barrier.
-__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-               "s"(base), "s"(lds_addr)
-               : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void *p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
-}
-
 // Wait for all of this wave's tile copies, then meet the other waves.
 __device__ __forceinline__ void tile_barrier() {
   constexpr int enc = (0x7 << 4) | (0xF << 8);  // vmcnt(0)

@@ -46,6 +46,25 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// One 16-byte global -> LDS copy per lane (gfx950's global-load-to-LDS): lane
+// l reads base + voff (bytes; base wave-uniform) and writes LDS bytes
+// lds_addr + 16 l (lds_addr wave-uniform). It is issued as an instruction the
+// compiler does not model: with such a copy in flight the compiler otherwise
+// waits for every outstanding LDS read at each use. Callers therefore await
+// completion themselves (s_waitcnt vmcnt before the barrier that publishes
+// the tile).
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(base), "s"(lds_addr)
+               : "memory");
+}
+
+// Byte address of an LDS object, as the wave-uniform value dma16 takes.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p);
+}
+
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 

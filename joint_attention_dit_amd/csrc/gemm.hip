@@ -10,16 +10,23 @@
 // features of one token: RoPE pairs (2i, 2i+1) sit in one lane and stores are
 // 8- or 16-byte vectors.
 //
-// Tiling: 256 features x 256 tokens per workgroup, K step 32 (two MFMA
-// k-steps of 16), four waves in a 2 x 2 arrangement, each owning 128 x 128
-// outputs (4 x 4 blocks of 32 x 32, 256 fp32 accumulators per lane).
-// Global tiles go straight into LDS (gfx950's 16-byte global-load-to-LDS)
-// through a 4-stage ring, three tiles ahead of the multiply, with one barrier
-// per K step. The fragments of the second k-step are read from LDS while the
-// first k-step's MFMAs run, and the next tile's first fragments while the
-// second k-step's run. LDS rows are 128 bytes; 16-byte chunk c of row r is
-// stored at chunk c ^ ((r >> 1) & 7), so the 16 rows read by a quarter-wave
-// fragment load cover all 64 banks.
+// Tiling: 256 features x 256 tokens per workgroup, K step 64 (four MFMA
+// k-steps of 16), eight waves (two per SIMD) in a 2 x 4 arrangement, each
+// owning 128 features x 64 tokens (4 x 2 blocks of 32 x 32, 128 fp32
+// accumulators per lane). With two waves per SIMD one wave's matrix cores
+// keep running while the other waits at the barrier or issues its copies.
+// Global tiles go straight into LDS (gfx950's 16-byte global-load-to-LDS),
+// double buffered, 64 KB per stage. Every tile row is one 128-byte segment of
+// a K-contiguous matrix row: copies of 64-byte segments reach only about half
+// the global-to-LDS rate per CU that this tile needs. The fragments of each
+// k-step are read from LDS while the previous k-step's MFMAs run. One barrier
+// per K step, after the first MFMAs of the last k-step: by then every wave has
+// read its last fragments of the current stage (so the stage can take the
+// tile after next) and the next tile has landed (so its first fragments are
+// read during the last k-step). The copies of a tile are spread over the MFMA
+// groups of two k-steps instead of issued in one burst. LDS rows are 128
+// bytes; 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), so
+// the 16 rows read by a quarter-wave fragment load cover all 64 banks.
 //
 // Workgroup order: the dispatcher hands workgroup i to XCD i % 8. The
 // linear id is remapped so that each XCD receives a contiguous range of
@@ -36,14 +43,14 @@ namespace {
 
 constexpr int BN = 256;   // weight rows (output features) per tile
 constexpr int BT = 256;   // activation rows (tokens) per tile
-constexpr int BK = 32;    // K per LDS stage
-constexpr int NSTAGE = 4; // LDS stages (tiles in flight: NSTAGE - 1 ahead)
-constexpr int TILE_ELEMS = 256 * BK;  // one operand tile, bf16 elements (16 KB)
+constexpr int BK = 64;    // K per LDS stage (128-byte rows)
+constexpr int NSTAGE = 2; // LDS stages
+constexpr int TILE_ELEMS = 256 * BK;  // one operand tile, bf16 elements (32 KB)
 constexpr int GROUP_T = 8;
 
-// LDS rows are 64 bytes (4 chunks of 16 B); 4 rows share one 256-byte bank line,
-// so chunk c of row r is stored at chunk c ^ ((r >> 2) & 3).
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 2) & 3); }
+// LDS rows are 128 bytes (8 chunks of 16 B); 2 rows share one 256-byte bank line,
+// so chunk c of row r is stored at chunk c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_n, int tiles_t,
                                             int &tn, int &tt) {
@@ -132,10 +139,9 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
   }
 }
 
-// Wait until at most N of this wave's global-to-LDS loads are still in flight
-// (they complete in issue order), then meet the other waves: afterwards every
-// wave's earlier loads have landed in LDS. No LDS instruction is waited for:
-// the tiles reach LDS only through these loads.
+// Wait until at most N of this wave's global-to-LDS copies are still in
+// flight (they complete in issue order), then meet the other waves: afterwards
+// every wave's earlier copies have landed in LDS.
 template <int N>
 __device__ __forceinline__ void tile_barrier() {
   // s_waitcnt vmcnt(N) (lgkmcnt and expcnt fields left at their maximum)
@@ -145,44 +151,44 @@ __device__ __forceinline__ void tile_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
+__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16 lds[NSTAGE * 2 * TILE_ELEMS];  // 128 KB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 1, wt = wave >> 1;
+  const int wn = wave & 1, wt = wave >> 1;  // 2 x 4 waves of 128 features x 64 tokens
   const int tiles_n = (int)ceil_div(a.N, BN), tiles_t = (int)ceil_div(a.M, BT);
   int tn, tt;
   tile_coords(blockIdx.x, gridDim.x, tiles_n, tiles_t, tn, tt);
   const int n0 = tn * BN, t0 = tt * BT;
 
-  // global -> LDS without registers: each wave fills 4 blocks of 1 KB (16 rows of
-  // 64 bytes) per operand tile; lane l lands at byte 16 l of its block, i.e. at
-  // row 16 b + l / 4, physical chunk l % 4, so it fetches logical chunk
-  // (l % 4) ^ swz(row). Rows past the matrix edge repeat the last row.
+  // global -> LDS without registers: each wave fills 4 blocks of 1 KB (8 rows of
+  // 128 bytes) per operand tile; lane l lands at byte 16 l of its block, i.e. at
+  // row 8 b + l / 8, physical chunk l % 8, so it fetches logical chunk
+  // (l % 8) ^ swz(row). Rows past the matrix edge repeat the last row.
   const char *wpanel = static_cast<const char *>(a.w) + (int64_t)n0 * a.K * 2;
   const char *xpanel = static_cast<const char *>(a.x) + (int64_t)t0 * a.K * 2;
   uint32_t woff[4], xoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int row = (wave * 4 + j) * 16 + (lane >> 2);
-    const int lc = swz(row, lane & 3);
+    const int row = (wave * 4 + j) * 8 + (lane >> 3);
+    const int lc = swz(row, lane & 7);
     woff[j] = (uint32_t)(min(n0 + row, a.N - 1) - n0) * (uint32_t)a.K * 2u + lc * 16u;
     xoff[j] = (uint32_t)(min(t0 + row, a.M - 1) - t0) * (uint32_t)a.K * 2u + lc * 16u;
   }
-  auto dload = [&](int stage, int k0) {
+  const uint32_t lds0 = lds_address(lds);
+  // copies j0 .. j1-1 of each operand of the tile at k0 into stage
+  auto dload_part = [&](int stage, int k0, int j0, int j1) {
     const char *wp = wpanel + (int64_t)k0 * 2;
     const char *xp = xpanel + (int64_t)k0 * 2;
-    bf16 *sw = lds + stage * 2 * TILE_ELEMS + wave * 4 * 512;
-    bf16 *sx = sw + TILE_ELEMS;
+    const uint32_t sw = lds0 + (uint32_t)(stage * 2 * TILE_ELEMS + wave * 4 * 512) * 2u;
+    const uint32_t sx = sw + TILE_ELEMS * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      __builtin_amdgcn_global_load_lds(wp + woff[j], (lds_void *)(sw + j * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(xp + xoff[j], (lds_void *)(sx + j * 512), 16, 0, 0);
+    for (int j = j0; j < j1; ++j) {
+      dma16(wp, woff[j], sw + j * 1024);
+      dma16(xp, xoff[j], sx + j * 1024);
     }
   };
 
@@ -190,117 +196,124 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(GemmArgs a) {
   // tile (k-step s of 16); the swizzle depends on r32 only, so block b sits at a
   // fixed offset of b * 32 rows
   const int r32 = lane & 31, kh = lane >> 5;
-  int fa_base[2], fb_base[2];
+  int fa_base[4], fb_base[4];
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < 4; ++s) {
     fa_base[s] = (wn * 128 + r32) * BK + (swz(r32, 2 * s + kh) * 8);
-    fb_base[s] = (wt * 128 + r32) * BK + (swz(r32, 2 * s + kh) * 8);
+    fb_base[s] = (wt * 64 + r32) * BK + (swz(r32, 2 * s + kh) * 8);
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int ktiles = a.K / BK;
 
-  // Fragments are double buffered; the next k-step's are all requested during
-  // the first half of the current one, so the wait before the next k-step is
-  // free.
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][4], fb[2][2];
   auto fload_all = [&](int stage, int s, int buf) {
     const bf16 *sw = lds + stage * 2 * TILE_ELEMS;
     const bf16 *sx = sw + TILE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fb[buf][i] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[s] + i * 32 * BK);
+    for (int j = 0; j < 2; ++j)
+      fb[buf][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[s] + j * 32 * BK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
       fa[buf][i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[s] + i * 32 * BK);
-    }
   };
-  // One k-step of 16 MFMAs on buffer BCUR. When NEXT, the fragments of the next
-  // k-step (LDS stage nstage, k-step ns) are fetched into the other buffer.
-  // When SYNC >= 0, the wave first waits (after the first 4 MFMAs) until at most
-  // SYNC of its tile loads are in flight and meets the other waves, so that
-  // the next tile is in LDS for everyone; with REFILL it then starts loading
-  // tile kt + NSTAGE - 1 into the stage that tile kt - 1 used.
-  auto kstep = [&](auto bcur_c, auto next_c, auto sync_c, auto refill_c, int nstage, int ns,
-                   int kt) {
-    constexpr int BCUR = decltype(bcur_c)::value, SYNC = decltype(sync_c)::value;
-    constexpr bool NEXT = decltype(next_c)::value, REFILL = decltype(refill_c)::value;
+  // One k-step of 8 MFMAs on buffer BCUR; the fragments of k-step ns of LDS
+  // stage nstage are fetched into the other buffer meanwhile. When SYNC, the
+  // wave meets the others after its first 2 MFMAs (the next tile has then
+  // landed everywhere and nobody reads this tile's stage again). DMA selects
+  // the copies issued between the MFMA groups: 1 = the first half of tile
+  // kt + 2 into this tile's stage (after the barrier), 2 = the second half of
+  // tile kt + 1 (begun in the previous K step). With RT the copies are issued
+  // only when the runtime flag dma_on is set.
+  auto kstep = [&](auto bcur_c, auto sync_c, auto dma_c, auto rt_c, bool dma_on, int nstage,
+                   int ns, int kt) {
+    constexpr int BCUR = decltype(bcur_c)::value, DMA = decltype(dma_c)::value;
+    constexpr bool SYNC = decltype(sync_c)::value, RT = decltype(rt_c)::value;
     const bf16 *sw = lds + nstage * 2 * TILE_ELEMS;
     const bf16 *sx = sw + TILE_ELEMS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[BCUR][i], fb[BCUR][j], acc[i][j]);
-      if constexpr (SYNC >= 0) {
-        if (i == 0) {
-          tile_barrier<SYNC>();
-          if constexpr (REFILL) dload((kt + NSTAGE - 1) & (NSTAGE - 1), (kt + NSTAGE - 1) * BK);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[BCUR][i], fb[BCUR][j], acc[i][j]);
+      if constexpr (SYNC) {
+        if (i == 0) tile_barrier<0>();
+      }
+      if (!RT || dma_on) {
+        if constexpr (DMA == 1) {
+          if (i == 1) dload_part(kt & 1, (kt + 2) * BK, 0, 1);
+          if (i == 2) dload_part(kt & 1, (kt + 2) * BK, 1, 2);
+        }
+        if constexpr (DMA == 2) {
+          if (i == 0) dload_part((kt + 1) & 1, (kt + 1) * BK, 2, 3);
+          if (i == 2) dload_part((kt + 1) & 1, (kt + 1) * BK, 3, 4);
         }
       }
-      if constexpr (NEXT) {
-        if (i < 2) {
+      if (i == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (i == 0)
-              fb[BCUR ^ 1][r] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + r * 32 * BK);
-            else
-              fa[BCUR ^ 1][r] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + r * 32 * BK);
-          }
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // 4 MFMA
-        if (i < 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
+        for (int j = 0; j < 2; ++j)
+          fb[BCUR ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + j * 32 * BK);
       }
+      if (i == 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          fa[BCUR ^ 1][r] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + r * 32 * BK);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (i == 1) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using S0 = std::integral_constant<int, 0>;
-  using S8 = std::integral_constant<int, 8>;
-  using NOSYNC = std::integral_constant<int, -1>;
+  using D0 = std::integral_constant<int, 0>;
+  using D1 = std::integral_constant<int, 1>;
+  using D2 = std::integral_constant<int, 2>;
   using Y = std::true_type;
   using N = std::false_type;
-  const int stage_mask = NSTAGE - 1;
 
-  // Pipeline: NSTAGE - 1 tiles in flight. Tile kt's second k-step waits (once)
-  // for tile kt+1 to land, then refills the stage of tile kt-1 with tile
-  // kt+NSTAGE-1 and reads tile kt+1's first fragments while it multiplies.
-  // The last tiles are peeled so that every wait count is a constant.
-#pragma unroll
-  for (int p = 0; p < NSTAGE - 1; ++p)
-    if (p < ktiles) dload(p, p * BK);
-  if (ktiles >= 3) tile_barrier<16>();
-  else if (ktiles == 2) tile_barrier<8>();
-  else tile_barrier<0>();
+  // One K step over the tile in stage kt & 1: k-steps 0..3, the last one with
+  // the barrier and the first fragments of tile kt + 1. Tile kt + 2 is copied
+  // into this stage in two halves: during k-step 3 (after the barrier) and
+  // during k-step 0 of the next K step. In the steady state every copy is
+  // present (RT false); the first and last K steps decide at run time. The
+  // last K step still reads (stale) fragments of the other stage and meets
+  // the other waves once more, which is harmless.
+  auto ktile = [&](auto rt_c, int kt) {
+    const bool tail = kt >= 1 && kt + 1 < ktiles;
+    const bool refill = kt + 2 < ktiles;
+    const int st = kt & 1;
+    kstep(I0(), N(), D2(), rt_c, tail, st, 1, kt);
+    kstep(I1(), N(), D0(), rt_c, false, st, 2, kt);
+    kstep(I0(), N(), D0(), rt_c, false, st, 3, kt);
+    kstep(I1(), Y(), D1(), rt_c, refill, st ^ 1, 0, kt);
+  };
+
+  dload_part(0, 0, 0, 4);
+  if (ktiles > 1) {
+    dload_part(1, BK, 0, 4);
+    tile_barrier<8>();
+  } else {
+    tile_barrier<0>();
+  }
   fload_all(0, 0, 0);
-  // settle every counter once (including scalar loads, which would otherwise
-  // make the compiler wait for all LDS reads at each k-step)
-  __builtin_amdgcn_s_waitcnt(0);
-  int kt = 0;
-  for (; kt + 3 < ktiles; ++kt) {
-    kstep(I0(), Y(), NOSYNC(), N(), kt & stage_mask, 1, kt);
-    kstep(I1(), Y(), S8(), Y(), (kt + 1) & stage_mask, 0, kt);
-  }
-  if (kt + 2 < ktiles) {  // tile kt+2 still in flight behind kt+1
-    kstep(I0(), Y(), NOSYNC(), N(), kt & stage_mask, 1, kt);
-    kstep(I1(), Y(), S8(), N(), (kt + 1) & stage_mask, 0, kt);
-    ++kt;
-  }
-  if (kt + 1 < ktiles) {  // only tile kt+1 in flight
-    kstep(I0(), Y(), NOSYNC(), N(), kt & stage_mask, 1, kt);
-    kstep(I1(), Y(), S0(), N(), (kt + 1) & stage_mask, 0, kt);
-    ++kt;
-  }
-  kstep(I0(), Y(), NOSYNC(), N(), kt & stage_mask, 1, kt);
-  kstep(I1(), N(), NOSYNC(), N(), 0, 0, kt);
+  // settle the scalar loads once (pending ones would make the compiler wait for
+  // all LDS reads at each k-step); copies stay in flight
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+  ktile(Y(), 0);
+  int kt = 1;
+  for (; kt + 2 < ktiles; ++kt) ktile(N(), kt);
+  for (; kt < ktiles; ++kt) ktile(Y(), kt);
 
-  const int nb = n0 + wn * 128 + 4 * kh, tb = t0 + wt * 128 + r32;
+  const int nb = n0 + wn * 128 + 4 * kh, tb = t0 + wt * 64 + r32;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -315,19 +328,19 @@ hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s) {
   const int tiles = (int)(ceil_div(a.N, BN) * ceil_div(a.M, BT));
   switch (epi) {
     case EPI_QKV_ROPE:
-      hipLaunchKernelGGL(gemm_kernel<EPI_QKV_ROPE>, dim3(tiles), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gemm_kernel<EPI_QKV_ROPE>, dim3(tiles), dim3(512), 0, s, a);
       break;
     case EPI_RESID_BF16:
-      hipLaunchKernelGGL(gemm_kernel<EPI_RESID_BF16>, dim3(tiles), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gemm_kernel<EPI_RESID_BF16>, dim3(tiles), dim3(512), 0, s, a);
       break;
     case EPI_RESID_F32:
-      hipLaunchKernelGGL(gemm_kernel<EPI_RESID_F32>, dim3(tiles), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gemm_kernel<EPI_RESID_F32>, dim3(tiles), dim3(512), 0, s, a);
       break;
     case EPI_GELU:
-      hipLaunchKernelGGL(gemm_kernel<EPI_GELU>, dim3(tiles), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gemm_kernel<EPI_GELU>, dim3(tiles), dim3(512), 0, s, a);
       break;
     case EPI_F32:
-      hipLaunchKernelGGL(gemm_kernel<EPI_F32>, dim3(tiles), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(gemm_kernel<EPI_F32>, dim3(tiles), dim3(512), 0, s, a);
       break;
   }
   return hipGetLastError();
