@@ -122,14 +122,114 @@ def summarize(cfg, ms, stage_ms):
     if dom in flops and dom != "modulation":
         ach = flops[dom] / t / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom), "traffic_unit": "HBM bytes per launch",
                 "algorithmic_per_launch": flops[dom]}
     else:
         ach = nbytes[dom] / t / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(dom), "traffic_unit": "HBM bytes per launch",
                 "algorithmic_per_launch": nbytes[dom]}
     return tflops, kernels, roof
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_4096.md")
+KERNEL_SOURCES = {
+    "attention": "attention.hip", "qkv_rope_gemm": "gemm.hip", "out_proj_gemm": "gemm.hip",
+    "mlp_up_gelu_gemm": "gemm.hip", "mlp_down_gemm": "gemm.hip", "modulation": "modulation.hip",
+    "rmsnorm1": "rmsnorm_modulate.hip", "rmsnorm2": "rmsnorm_modulate.hip",
+    "rope_table": "rope_table.hip",
+}
+# dispatch order of one block forward (h3dit_block_forward launches in this order)
+KERNEL_ORDER = ["modulation", "rope_table", "rmsnorm1", "qkv_rope_gemm", "attention",
+                "out_proj_gemm", "rmsnorm2", "mlp_up_gelu_gemm", "mlp_down_gemm"]
+COPY_BYTES = 1 << 30   # the plain copy used to calibrate the HBM byte counters
+
+
+def source_digest(stage: str) -> str:
+    import hashlib
+    path = os.path.join(ROOT, "joint_attention_dit_amd", "csrc", KERNEL_SOURCES[stage])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(stage: str):
+    """HBM bytes per launch of `stage` from the committed counter summary, or None
+    when the summary is missing or the kernel's source changed since it was taken."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        blob = text.split("```json", 1)[1].split("```", 1)[0]
+        rec = json.loads(blob)["kernels"][stage]
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_digest(stage):
+        return None
+    return rec["hbm_bytes"]
+
+
+def traffic_run(cfg):
+    """One plain 1 GiB device copy, then one block forward: the command that the
+    two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE) profile."""
+    import torch
+    from joint_attention_dit_amd import binding as B
+    from joint_attention_dit_amd.inputs import make_inputs
+
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    inp = make_inputs(cfg, seed=0)
+    blk = B.Block(cfg, inp, device="cuda:0")
+    del inp
+    blk.forward(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    print("traffic run done", flush=True)
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, cfg) -> str:
+    """Counter CSVs of the two traffic-run passes -> the profiles/ summary text."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        rows.sort()
+        return rows
+
+    out = {}
+    scales = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = per_dispatch(d, counter)
+        copy = [r for r in rows if "copy" in r[1].lower() or "elementwise" in r[1].lower()]
+        lib = [r for r in rows if "h3dit" in r[1]]
+        assert copy and len(lib) >= len(KERNEL_ORDER), (counter, len(copy), len(lib))
+        copy_kib = max(r[2] for r in copy)
+        scales[counter] = COPY_BYTES / (copy_kib * 1024.0)
+        for stage, r in zip(KERNEL_ORDER, lib[-len(KERNEL_ORDER):]):
+            out.setdefault(stage, {})[counter] = r[2]
+    kernels = {}
+    for stage, v in out.items():
+        b = v["FETCH_SIZE"] * 1024 * scales["FETCH_SIZE"] + v["WRITE_SIZE"] * 1024 * scales["WRITE_SIZE"]
+        kernels[stage] = {"fetch_kib": v["FETCH_SIZE"], "write_kib": v["WRITE_SIZE"],
+                          "hbm_bytes": round(b), "source_sha256_16": source_digest(stage)}
+    rec = {"workload": cfg.description, "copy_bytes": COPY_BYTES,
+           "scale_fetch": round(scales["FETCH_SIZE"], 4), "scale_write": round(scales["WRITE_SIZE"], 4),
+           "kernels": kernels}
+    flops, nbytes = stage_work(cfg)
+    lines = ["| Kernel | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) | algorithmic bytes |",
+             "|---|---|---|---|---|"]
+    for stage in KERNEL_ORDER:
+        k = kernels[stage]
+        lines.append(f"| {stage} | {k['fetch_kib']:.0f} | {k['write_kib']:.0f} | "
+                     f"{k['hbm_bytes'] / 1e6:.1f} MB | {nbytes[stage] / 1e6:.1f} MB |")
+    return "\n".join(lines) + "\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n"
 
 
 def cpu_baseline(cfg, rows: int):
@@ -180,7 +280,16 @@ def main():
     ap.add_argument("--extra", default="2048", help="second workload reported under 'extra' ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="one 1 GiB copy + one block (the command the HBM counter passes profile)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn the two counter passes into the profiles/ summary table (host only)")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        from joint_attention_dit_amd.inputs import CONFIGS
+        print(summarize_traffic(*args.summarize_traffic, CONFIGS[args.workload]))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the block runs on a single MI355X and this build "
@@ -192,6 +301,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     cfg = CONFIGS[args.workload]
+    if args.traffic_run:
+        traffic_run(cfg)
+        return
     ms, stage_ms, ok = measure(cfg, args.steps, args.warmup)
     tflops, kernels, roof = summarize(cfg, ms, stage_ms)
 
