@@ -2,20 +2,29 @@
 // and shifted by the AdaLN modulation). One wavefront per token row:
 //   pass 1: sum of squares in fp64 (squares of bf16 / fp32 values are exact);
 //   pass 2: h = x * r * (1 + scale) + shift in fp64, one rounding to bf16.
-// The second pass re-reads the row (an L2 hit), so HBM traffic is one read
-// of x and one write of h.
+// For rows of up to 8192 elements the row stays in registers between the
+// passes, so x is read from memory once (with thousands of rows in flight the
+// L2 does not keep a row until its second pass); longer rows are read twice.
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace h3dit {
 
 template <typename XT>
 struct Chunk8;
 
+// 8 consecutive elements kept in their storage type (bf16: 4 registers)
 template <>
 struct Chunk8<bf16> {
+  typedef bf16x8 raw;
+  static __device__ __forceinline__ raw fetch(const bf16 *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
+  }
+  static __device__ __forceinline__ float at(const raw &r, int j) { return (float)r[j]; }
   static __device__ __forceinline__ void load(const bf16 *p, float v[8]) {
-    const bf16x8 t = *reinterpret_cast<const bf16x8 *>(p);
+    const raw t = fetch(p);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (float)t[j];
   }
@@ -23,17 +32,71 @@ struct Chunk8<bf16> {
 
 template <>
 struct Chunk8<float> {
+  struct raw {
+    f32x4 a, b;
+  };
+  static __device__ __forceinline__ raw fetch(const float *p) {
+    return raw{*reinterpret_cast<const f32x4 *>(p), *reinterpret_cast<const f32x4 *>(p + 4)};
+  }
+  static __device__ __forceinline__ float at(const raw &r, int j) { return j < 4 ? r.a[j] : r.b[j - 4]; }
   static __device__ __forceinline__ void load(const float *p, float v[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+    const raw t = fetch(p);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[j] = a[j];
-      v[4 + j] = b[j];
-    }
+    for (int j = 0; j < 8; ++j) v[j] = at(t, j);
   }
 };
 
+// Row in registers: lane l holds 16-byte chunks l, l + 64, ... (at most NC).
+template <typename XT, int NC>
+__global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(const XT *__restrict__ x,
+                                                                   const double *__restrict__ shift,
+                                                                   const double *__restrict__ scale,
+                                                                   bf16 *__restrict__ h, int T,
+                                                                   int D, double eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= T) return;
+  const XT *xr = x + (int64_t)row * D;
+  bf16 *hr = h + (int64_t)row * D;
+  const int chunks = D >> 3;
+
+  typename Chunk8<XT>::raw v[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) v[i] = Chunk8<XT>::fetch(xr + c * 8);
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    if (lane + 64 * i < chunks) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double e = (double)Chunk8<XT>::at(v[i], j);
+        ss += e * e;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  const double r = 1.0 / sqrt(ss / (double)D + eps);
+
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      bf16x8 o;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = c * 8 + j;
+        o[j] = to_bf16((double)Chunk8<XT>::at(v[i], j) * r * (1.0 + scale[col]) + shift[col]);
+      }
+      *reinterpret_cast<bf16x8 *>(hr + c * 8) = o;
+    }
+  }
+}
+
+// Longer rows: two passes over memory.
 template <typename XT>
 __global__ __launch_bounds__(256) void rmsnorm_modulate_kernel(const XT *__restrict__ x,
                                                                const double *__restrict__ shift,
@@ -75,6 +138,24 @@ hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *s
                                    const double *scale, void *h, int T, int D, float eps,
                                    hipStream_t s) {
   const int blocks = (int)ceil_div(T, 4);
+  auto reg = [&](auto nc_c) {
+    constexpr int NC = decltype(nc_c)::value;
+    if (x_is_f32)
+      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<float, NC>), dim3(blocks), dim3(256), 0, s,
+                         static_cast<const float *>(x), shift, scale, static_cast<bf16 *>(h), T, D,
+                         (double)eps);
+    else
+      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<bf16, NC>), dim3(blocks), dim3(256), 0, s,
+                         static_cast<const bf16 *>(x), shift, scale, static_cast<bf16 *>(h), T, D,
+                         (double)eps);
+    return hipGetLastError();
+  };
+  const int per_lane = (int)ceil_div(D, 64 * 8);  // 16-byte chunks per lane
+  if (per_lane <= 1) return reg(std::integral_constant<int, 1>());
+  if (per_lane <= 4) return reg(std::integral_constant<int, 4>());
+  if (per_lane <= 8) return reg(std::integral_constant<int, 8>());
+  if (per_lane <= 11) return reg(std::integral_constant<int, 11>());
+  if (per_lane <= 16) return reg(std::integral_constant<int, 16>());
   if (x_is_f32)
     hipLaunchKernelGGL(rmsnorm_modulate_kernel<float>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const float *>(x), shift, scale, static_cast<bf16 *>(h), T, D,
