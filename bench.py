@@ -232,6 +232,53 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cfg) -> str:
     return "\n".join(lines) + "\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n"
 
 
+def measure_stack(scfg, images: int, warmup: int):
+    """Seconds per image of DiT compute: `scfg.steps` evaluations of the whole
+    stack (patch embedding, n_blocks blocks, final layer) with an Euler update
+    after each, on seeded random-init weights resident in HBM."""
+    import torch
+    from joint_attention_dit_amd import binding as B
+    from joint_attention_dit_amd.inputs import make_stack_inputs
+
+    inp = make_stack_inputs(scfg, seed=0, device="cuda")
+    cfg = B.config_from(scfg.block)
+    gh, gw = scfg.grid
+    st = B.StackConfig(scfg.n_blocks, scfg.channels, scfg.patch, gh, gw, scfg.block.text_tokens)
+    ws = torch.empty(B.h3dit_stack_workspace_size(cfg, st), dtype=torch.uint8, device="cuda")
+    latent0 = inp["latent"].clone()
+    latent = latent0.clone()
+    v = torch.empty_like(latent)
+    stream = torch.cuda.current_stream()
+
+    def image():
+        latent.copy_(latent0)
+        for cond in inp["conds"]:
+            B.h3dit_dit_forward(cfg, st, inp["w_patch"], inp["w_ada_final"], inp["w_final"],
+                                inp["blocks"], latent, inp["text"], cond, inp["positions"], v, ws,
+                                stream)
+            B.h3dit_latent_step(latent, v, 1.0 / scfg.steps, stream)
+
+    for _ in range(warmup):
+        image()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(images):
+        image()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    sec = t0.elapsed_time(t1) / 1e3 / images
+    ok = bool(torch.isfinite(latent).all().item())
+    return sec, ok
+
+
+def stack_flops(scfg) -> float:
+    b = scfg.block
+    per_eval = scfg.n_blocks * block_flops(b) + 2.0 * 2 * b.image_tokens * b.hidden * scfg.patch_features \
+        + 2.0 * 2 * b.hidden * b.hidden
+    return per_eval * scfg.steps
+
+
 def cpu_baseline(cfg, rows: int):
     """Time the float64 oracle on the same block at 1 and at `rows` sampled query rows.
 
@@ -280,6 +327,8 @@ def main():
     ap.add_argument("--extra", default="2048", help="second workload reported under 'extra' ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
+    ap.add_argument("--stack", action="store_true",
+                    help="time the full DiT stack (50 blocks, 6 steps at 2048x2048) instead")
     ap.add_argument("--traffic-run", action="store_true",
                     help="one 1 GiB copy + one block (the command the HBM counter passes profile)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -303,6 +352,23 @@ def main():
     cfg = CONFIGS[args.workload]
     if args.traffic_run:
         traffic_run(cfg)
+        return
+    if args.stack:
+        from joint_attention_dit_amd.inputs import STACK_CONFIGS
+        scfg = STACK_CONFIGS["dit_2048"]
+        sec, ok = measure_stack(scfg, images=max(args.steps // 10, 1), warmup=1 if args.warmup else 0)
+        fl = stack_flops(scfg)
+        print(json.dumps({
+            "metric": "DiT compute images/s (50 blocks x 6 denoising steps, 2048x2048)",
+            "value": round(1.0 / sec, 4), "unit": "images/s", "n_gpus": 1,
+            "ms_per_image": round(sec * 1e3, 2),
+            "ms_per_block": round(sec * 1e3 / (scfg.n_blocks * scfg.steps), 4),
+            "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded, drawn on the GPU)",
+            "config": {"workload": scfg.description, "n_blocks": scfg.n_blocks, "steps": scfg.steps,
+                       "n_tokens": scfg.block.n_tokens, "latent": list(scfg.latent_shape)},
+            "tflops": round(fl / sec / 1e12, 1),
+            "pct_bf16_mfma_peak": round(100 * fl / sec / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "output_finite": ok}), flush=True)
         return
     ms, stage_ms, ok = measure(cfg, args.steps, args.warmup)
     tflops, kernels, roof = summarize(cfg, ms, stage_ms)

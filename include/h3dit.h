@@ -177,6 +177,58 @@ int h3dit_mlp_down_residual(const h3dit_config *cfg, const void *u, const void *
 int h3dit_linear_f32(const void *x, const void *w, int32_t M, int32_t N, int32_t K, float *y,
                      void *stream);
 
+/* ---------------------------------------------------------------------------
+ * The DiT stack around the blocks (model card, "Model Architecture": latents
+ * cut into patches become the image tokens of the packed sequence; spec page,
+ * "Specifications": 50 layers). One DiT evaluation, for a latent [C, H, W]
+ * with patch size p (gh = H / p, gw = W / p image-token rows and columns):
+ *   patch(t)[c*p*p + dy*p + dx] = latent[c, gy*p + dy, gx*p + dx],  t = gy*gw + gx
+ *   x        = [ text ; patch . w_patch^T ]                  fp32 [T, D]
+ *   x        = block_{n-1}( ... block_0(x) ... ), every block with the same cond
+ *   (shift, scale) = w_ada_final . cond                      (fp64, like the blocks)
+ *   vt(t)    = (rmsnorm(x_img(t)) * (1 + scale) + shift) . w_final^T   fp32, image tokens
+ *   v[c, y, x] = vt(t of (y / p, x / p))[c*p*p + (y % p)*p + x % p]
+ * The patch embedding and the final projection are fp32 (no matrix-core
+ * rounding); the blocks run exactly as h3dit_block_forward with fp32 x.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    int32_t n_blocks;     /* number of blocks (50 for the full model; 0 allowed)        */
+    int32_t channels;     /* C: latent channels (24)                                    */
+    int32_t patch;        /* p: patch size (2)                                          */
+    int32_t grid_h;       /* gh: image-token rows                                       */
+    int32_t grid_w;       /* gw: image-token columns                                    */
+    int32_t text_tokens;  /* text tokens at the front of the sequence                   */
+} h3dit_stack_config;
+
+typedef struct {
+    const float *w_patch;        /* fp32 [D, C*p*p]                                     */
+    const void *w_ada_final;     /* bf16 [2D, D]  rows: shift | scale                   */
+    const float *w_final;        /* fp32 [C*p*p, D]                                     */
+    const h3dit_weights *blocks; /* host array of n_blocks block weight sets            */
+} h3dit_stack_weights;
+
+/* Bytes of device workspace h3dit_dit_forward needs (host-only, no HIP call).
+ * cfg->n_tokens must equal text_tokens + grid_h * grid_w; C*p*p must be a
+ * multiple of 4. */
+int h3dit_stack_workspace_size(const h3dit_config *cfg, const h3dit_stack_config *st,
+                               size_t *bytes);
+
+/* One DiT evaluation (see above).
+ *   latent     [C, gh*p, gw*p] fp32
+ *   text       [text_tokens, D] fp32 (may be NULL when text_tokens == 0)
+ *   cond       [D] fp32
+ *   positions  [T, 2] int32 RoPE positions of the packed sequence
+ *   v          [C, gh*p, gw*p] fp32; must not overlap the workspace
+ * cfg->x_dtype is ignored (the residual stream between blocks is fp32). */
+int h3dit_dit_forward(const h3dit_config *cfg, const h3dit_stack_config *st,
+                      const h3dit_stack_weights *w, const float *latent, const float *text,
+                      const float *cond, const int32_t *positions, float *v, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+/* latent[i] += dt * v[i] for i < n (fp32): the explicit Euler update between
+ * denoising steps. */
+int h3dit_latent_step(float *latent, const float *v, float dt, int64_t n, void *stream);
+
 /* Padded token count used by the vt layout (T rounded up to a multiple of 64). */
 int64_t h3dit_padded_tokens(int64_t n_tokens);
 

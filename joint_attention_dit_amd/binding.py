@@ -25,7 +25,8 @@ EXPORTED = (
     "h3dit_workspace_size", "h3dit_block_forward", "h3dit_block_forward_timed",
     "h3dit_modulation", "h3dit_rmsnorm_modulate", "h3dit_rope_table", "h3dit_qkv_rope",
     "h3dit_attention", "h3dit_out_proj_residual", "h3dit_mlp_up_gelu",
-    "h3dit_mlp_down_residual", "h3dit_linear_f32", "h3dit_padded_tokens", "h3dit_status_string",
+    "h3dit_mlp_down_residual", "h3dit_linear_f32", "h3dit_stack_workspace_size",
+    "h3dit_dit_forward", "h3dit_latent_step", "h3dit_padded_tokens", "h3dit_status_string",
     "h3dit_last_error",
 )
 
@@ -47,6 +48,17 @@ class Weights(ctypes.Structure):
     _fields_ = [("w_ada", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p),
                 ("w_o", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p)]
+
+
+class StackConfig(ctypes.Structure):
+    _fields_ = [("n_blocks", ctypes.c_int32), ("channels", ctypes.c_int32),
+                ("patch", ctypes.c_int32), ("grid_h", ctypes.c_int32),
+                ("grid_w", ctypes.c_int32), ("text_tokens", ctypes.c_int32)]
+
+
+class StackWeights(ctypes.Structure):
+    _fields_ = [("w_patch", ctypes.c_void_p), ("w_ada_final", ctypes.c_void_p),
+                ("w_final", ctypes.c_void_p), ("blocks", ctypes.POINTER(Weights))]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -76,6 +88,10 @@ def load_library() -> ctypes.CDLL:
         "h3dit_mlp_up_gelu": [cfgp, vp, vp, vp, vp],
         "h3dit_mlp_down_residual": [cfgp, vp, vp, vp, vp, vp, vp],
         "h3dit_linear_f32": [vp, vp, i32, i32, i32, vp, vp],
+        "h3dit_stack_workspace_size": [cfgp, ctypes.POINTER(StackConfig), ctypes.POINTER(sz)],
+        "h3dit_dit_forward": [cfgp, ctypes.POINTER(StackConfig), ctypes.POINTER(StackWeights),
+                              vp, vp, vp, vp, vp, vp, sz, vp],
+        "h3dit_latent_step": [vp, vp, ctypes.c_float, ctypes.c_int64, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -219,6 +235,31 @@ def h3dit_linear_f32(x: torch.Tensor, w: torch.Tensor, y: torch.Tensor, stream=N
     N = w.shape[0]
     _check(load_library().h3dit_linear_f32(_ptr(x), _ptr(w), M, N, K, _ptr(y), _stream(stream)),
            "h3dit_linear_f32")
+
+
+def h3dit_stack_workspace_size(cfg: Config, st: StackConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().h3dit_stack_workspace_size(ctypes.byref(cfg), ctypes.byref(st),
+                                                     ctypes.byref(n)),
+           "h3dit_stack_workspace_size")
+    return n.value
+
+
+def h3dit_dit_forward(cfg: Config, st: StackConfig, w_patch, w_ada_final, w_final,
+                      blocks: Sequence[Dict[str, torch.Tensor]], latent, text, cond, positions,
+                      v, workspace, stream=None) -> None:
+    arr = (Weights * max(len(blocks), 1))(*[weights_struct(b) for b in blocks])
+    sw = StackWeights(_ptr(w_patch), _ptr(w_ada_final), _ptr(w_final),
+                      ctypes.cast(arr, ctypes.POINTER(Weights)))
+    _check(load_library().h3dit_dit_forward(
+        ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), _ptr(latent), _ptr(text),
+        _ptr(cond), _ptr(positions), _ptr(v), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "h3dit_dit_forward")
+
+
+def h3dit_latent_step(latent: torch.Tensor, v: torch.Tensor, dt: float, stream=None) -> None:
+    _check(load_library().h3dit_latent_step(_ptr(latent), _ptr(v), float(dt), latent.numel(),
+                                            _stream(stream)), "h3dit_latent_step")
 
 
 # ------------------------------------------------------------------ helpers

@@ -234,9 +234,158 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   return ok();
 }
 
+struct StackPlan {
+  int64_t T, D, Ti, F;  // tokens, hidden, image tokens, features per patch
+  size_t block, xa, xb, patches, modf, hf, vt, total;
+  size_t block_bytes;
+};
+
+int check_stack(const h3dit_config *cfg, const h3dit_stack_config *st) {
+  CHECK_CFG(cfg);
+  if (!st) return fail(H3DIT_EINVAL, "st is NULL");
+  if (st->n_blocks < 0 || st->channels < 1 || st->patch < 1 || st->grid_h < 1 || st->grid_w < 1 ||
+      st->text_tokens < 0)
+    return fail(H3DIT_EINVAL, "stack config: need n_blocks >= 0, channels, patch, grid >= 1, "
+                "text_tokens >= 0");
+  const int64_t F = (int64_t)st->channels * st->patch * st->patch;
+  if (F % 4 != 0 || F > 65536)
+    return fail(H3DIT_EUNSUPPORTED, "channels * patch^2 must be a multiple of 4 up to 65536 "
+                "(got %lld)", (long long)F);
+  if ((int64_t)st->text_tokens + (int64_t)st->grid_h * st->grid_w != cfg->n_tokens)
+    return fail(H3DIT_EINVAL, "n_tokens (%d) must equal text_tokens + grid_h * grid_w", cfg->n_tokens);
+  return H3DIT_OK;
+}
+
+h3dit_config stack_block_config(const h3dit_config *cfg) {
+  h3dit_config c = *cfg;
+  c.x_dtype = H3DIT_F32;
+  return c;
+}
+
+StackPlan make_stack_plan(const h3dit_config *cfg, const h3dit_stack_config *st) {
+  StackPlan p;
+  p.T = cfg->n_tokens;
+  p.D = cfg->hidden;
+  p.Ti = (int64_t)st->grid_h * st->grid_w;
+  p.F = (int64_t)st->channels * st->patch * st->patch;
+  const h3dit_config bc = stack_block_config(cfg);
+  p.block_bytes = make_plan(&bc).total;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  p.block = take(p.block_bytes);
+  p.xa = take(4 * p.T * p.D);
+  p.xb = take(4 * p.T * p.D);
+  p.patches = take(4 * p.Ti * p.F);
+  p.modf = take(sizeof(double) * 2 * p.D);
+  p.hf = take(4 * p.Ti * p.D);
+  p.vt = take(4 * p.Ti * p.F);
+  p.total = off;
+  return p;
+}
+
+int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_stack_weights *w,
+             const float *latent, const float *text, const float *cond, const int32_t *positions,
+             float *v, void *ws, size_t ws_bytes, void *stream) {
+  {
+    const int st_ = check_stack(cfg, st);
+    if (st_ != H3DIT_OK) return st_;
+  }
+  if (!w) return fail(H3DIT_EINVAL, "w is NULL");
+  CHECK_PTR(w->w_patch);
+  CHECK_PTR(w->w_ada_final);
+  CHECK_PTR(w->w_final);
+  if (st->n_blocks > 0 && !w->blocks) return fail(H3DIT_EINVAL, "w->blocks is NULL");
+  CHECK_PTR(latent);
+  if (st->text_tokens > 0) CHECK_PTR(text);
+  CHECK_PTR(cond);
+  CHECK_PTR(positions);
+  CHECK_PTR(v);
+  CHECK_PTR(ws);
+  const StackPlan p = make_stack_plan(cfg, st);
+  if (ws_bytes < p.total)
+    return fail(H3DIT_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.total);
+  {
+    const size_t vb = 4 * (size_t)(p.Ti * p.F);
+    const char *vs = reinterpret_cast<const char *>(v), *wss = static_cast<const char *>(ws);
+    if (vs < wss + p.total && wss < vs + vb) return fail(H3DIT_EINVAL, "v overlaps workspace");
+  }
+  for (int l = 0; l < st->n_blocks; ++l) {  // every block's weights, before anything is enqueued
+    const h3dit_weights &b = w->blocks[l];
+    if (!b.w_ada || !b.w_qkv || !b.w_o || !b.w_up || !b.w_down)
+      return fail(H3DIT_EINVAL, "block %d has a NULL weight pointer", l);
+    if (!aligned16(b.w_ada) || !aligned16(b.w_qkv) || !aligned16(b.w_o) || !aligned16(b.w_up) ||
+        !aligned16(b.w_down))
+      return fail(H3DIT_EALIGN, "block %d has a weight pointer that is not 16-byte aligned", l);
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = (int)p.D, Ti = (int)p.Ti, F = (int)p.F, text_tokens = st->text_tokens;
+  float *xa = at<float>(ws, p.xa), *xb = at<float>(ws, p.xb);
+  float *patches = at<float>(ws, p.patches), *hf = at<float>(ws, p.hf), *vt = at<float>(ws, p.vt);
+  double *modf = at<double>(ws, p.modf);
+
+  // x = [text ; patch embedding]
+  if (text_tokens > 0)
+    LAUNCH(hipMemcpyAsync(xa, text, 4 * (size_t)text_tokens * D, hipMemcpyDeviceToDevice, s),
+           "text copy");
+  LAUNCH(launch_patchify(latent, patches, st->channels, st->patch, st->grid_h, st->grid_w, s),
+         "patchify");
+  LAUNCH(launch_gemm_f32(patches, w->w_patch, xa + (size_t)text_tokens * D, Ti, D, F, D, s),
+         "patch embedding");
+  // the blocks, ping-ponging the fp32 residual stream
+  const h3dit_config bc = stack_block_config(cfg);
+  float *cur = xa, *nxt = xb;
+  for (int l = 0; l < st->n_blocks; ++l) {
+    const int rc = forward_impl(&bc, cur, cond, &w->blocks[l], positions, nxt, at<void>(ws, p.block),
+                                p.block_bytes, stream, nullptr, 0);
+    if (rc != H3DIT_OK) return rc;
+    float *t = cur;
+    cur = nxt;
+    nxt = t;
+  }
+  // final layer on the image tokens
+  LAUNCH(launch_modulation(w->w_ada_final, cond, modf, 2 * D, D, s), "final modulation");
+  LAUNCH(launch_rmsnorm_modulate_f32out(cur + (size_t)text_tokens * D, true, modf, modf + D, hf, Ti,
+                                        D, cfg->eps, s),
+         "final rmsnorm");
+  LAUNCH(launch_gemm_f32(hf, w->w_final, vt, Ti, F, D, F, s), "final projection");
+  LAUNCH(launch_unpatchify(vt, v, st->channels, st->patch, st->grid_h, st->grid_w, s), "unpatchify");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
+
+int h3dit_stack_workspace_size(const h3dit_config *cfg, const h3dit_stack_config *st,
+                               size_t *bytes) {
+  const int rc = check_stack(cfg, st);
+  if (rc != H3DIT_OK) return rc;
+  if (!bytes) return fail(H3DIT_EINVAL, "bytes is NULL");
+  *bytes = make_stack_plan(cfg, st).total;
+  return ok();
+}
+
+int h3dit_dit_forward(const h3dit_config *cfg, const h3dit_stack_config *st,
+                      const h3dit_stack_weights *w, const float *latent, const float *text,
+                      const float *cond, const int32_t *positions, float *v, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  return dit_impl(cfg, st, w, latent, text, cond, positions, v, workspace, workspace_bytes, stream);
+}
+
+int h3dit_latent_step(float *latent, const float *v, float dt, int64_t n, void *stream) {
+  CHECK_PTR(latent);
+  CHECK_PTR(v);
+  if (n < 1) return fail(H3DIT_EINVAL, "n must be >= 1 (got %lld)", (long long)n);
+  if (!(dt == dt)) return fail(H3DIT_EINVAL, "dt is NaN");
+  LAUNCH(launch_latent_step(latent, v, dt, n, static_cast<hipStream_t>(stream)), "latent step");
+  return ok();
+}
+
 
 int64_t h3dit_padded_tokens(int64_t n_tokens) { return (n_tokens + 63) / 64 * 64; }
 

@@ -16,6 +16,11 @@ hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *s
                                    const double *scale, void *h, int T, int D, float eps,
                                    hipStream_t s);
 
+// same, fp32 output (the final layer of the DiT stack)
+hipError_t launch_rmsnorm_modulate_f32out(const void *x, bool x_is_f32, const double *shift,
+                                          const double *scale, float *h, int T, int D, float eps,
+                                          hipStream_t s);
+
 // table[T, 64] float2 (cos, sin)
 hipError_t launch_rope_table(const int32_t *pos, float *table, int T, float base, hipStream_t s);
 
@@ -40,5 +45,24 @@ hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s);
 // o[T, A] = attention over qk [T, 2A] and vt [H, 128, Tp]
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
                             hipStream_t s);
+
+// ---- DiT stack (patch-embed, final layer, latent update) ----
+
+// patches[gh * gw, C * p * p] fp32 from latent [C, gh * p, gw * p] fp32; token t = gy * gw + gx,
+// feature c * p * p + dy * p + dx
+hipError_t launch_patchify(const float *latent, float *patches, int C, int p, int gh, int gw,
+                           hipStream_t s);
+
+// latent-shaped v [C, gh * p, gw * p] from per-token rows vt [gh * gw, C * p * p] (inverse of
+// patchify)
+hipError_t launch_unpatchify(const float *vt, float *v, int C, int p, int gh, int gw,
+                             hipStream_t s);
+
+// y[M, N] (row stride ldy) = a[M, K] . b[N, K]^T, all fp32; K % 4 == 0
+hipError_t launch_gemm_f32(const float *a, const float *b, float *y, int M, int N, int K, int ldy,
+                           hipStream_t s);
+
+// latent[i] += dt * v[i], i < n
+hipError_t launch_latent_step(float *latent, const float *v, float dt, int64_t n, hipStream_t s);
 
 }  // namespace h3dit

@@ -2,7 +2,8 @@
 // and shifted by the AdaLN modulation). One wavefront per token row:
 //   pass 1: sum of squares in fp64 (squares of bf16 / fp32 values are exact);
 //   pass 2: h = x * r * (1 + scale) + shift in fp64, one rounding to bf16.
-// For rows of up to 8192 elements the row stays in registers between the
+// The output is bf16 (a matrix-core operand) or, for the final layer of the
+// DiT stack, fp32. For rows of up to 8192 elements the row stays in registers between the
 // passes, so x is read from memory once (with thousands of rows in flight the
 // L2 does not keep a row until its second pass); longer rows are read twice.
 #include "common.h"
@@ -46,18 +47,40 @@ struct Chunk8<float> {
   }
 };
 
+// Store 8 consecutive results (fp64) as bf16 (one rounding) or fp32.
+template <typename OT>
+__device__ __forceinline__ void store8(OT *p, const double v[8]);
+template <>
+__device__ __forceinline__ void store8<bf16>(bf16 *p, const double v[8]) {
+  bf16x8 o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = to_bf16(v[j]);
+  *reinterpret_cast<bf16x8 *>(p) = o;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float *p, const double v[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = (float)v[j];
+    b[j] = (float)v[4 + j];
+  }
+  *reinterpret_cast<f32x4 *>(p) = a;
+  *reinterpret_cast<f32x4 *>(p + 4) = b;
+}
+
 // Row in registers: lane l holds 16-byte chunks l, l + 64, ... (at most NC).
-template <typename XT, int NC>
+template <typename XT, int NC, typename OT>
 __global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(const XT *__restrict__ x,
                                                                    const double *__restrict__ shift,
                                                                    const double *__restrict__ scale,
-                                                                   bf16 *__restrict__ h, int T,
+                                                                   OT *__restrict__ h, int T,
                                                                    int D, double eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
   const XT *xr = x + (int64_t)row * D;
-  bf16 *hr = h + (int64_t)row * D;
+  OT *hr = h + (int64_t)row * D;
   const int chunks = D >> 3;
 
   typename Chunk8<XT>::raw v[NC];
@@ -85,29 +108,29 @@ __global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(const XT *__r
   for (int i = 0; i < NC; ++i) {
     const int c = lane + 64 * i;
     if (c < chunks) {
-      bf16x8 o;
+      double o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int col = c * 8 + j;
-        o[j] = to_bf16((double)Chunk8<XT>::at(v[i], j) * r * (1.0 + scale[col]) + shift[col]);
+        o[j] = (double)Chunk8<XT>::at(v[i], j) * r * (1.0 + scale[col]) + shift[col];
       }
-      *reinterpret_cast<bf16x8 *>(hr + c * 8) = o;
+      store8<OT>(hr + c * 8, o);
     }
   }
 }
 
 // Longer rows: two passes over memory.
-template <typename XT>
+template <typename XT, typename OT>
 __global__ __launch_bounds__(256) void rmsnorm_modulate_kernel(const XT *__restrict__ x,
                                                                const double *__restrict__ shift,
                                                                const double *__restrict__ scale,
-                                                               bf16 *__restrict__ h, int T, int D,
+                                                               OT *__restrict__ h, int T, int D,
                                                                double eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
   const XT *xr = x + (int64_t)row * D;
-  bf16 *hr = h + (int64_t)row * D;
+  OT *hr = h + (int64_t)row * D;
   const int chunks = D >> 3;
 
   double ss = 0.0;
@@ -124,30 +147,28 @@ __global__ __launch_bounds__(256) void rmsnorm_modulate_kernel(const XT *__restr
   for (int c = lane; c < chunks; c += 64) {
     float v[8];
     Chunk8<XT>::load(xr + c * 8, v);
-    bf16x8 o;
+    double o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int col = c * 8 + j;
-      o[j] = to_bf16((double)v[j] * r * (1.0 + scale[col]) + shift[col]);
+      o[j] = (double)v[j] * r * (1.0 + scale[col]) + shift[col];
     }
-    *reinterpret_cast<bf16x8 *>(hr + c * 8) = o;
+    store8<OT>(hr + c * 8, o);
   }
 }
 
-hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *shift,
-                                   const double *scale, void *h, int T, int D, float eps,
-                                   hipStream_t s) {
+template <typename OT>
+static hipError_t launch_rn(const void *x, bool x_is_f32, const double *shift, const double *scale,
+                            OT *h, int T, int D, float eps, hipStream_t s) {
   const int blocks = (int)ceil_div(T, 4);
   auto reg = [&](auto nc_c) {
     constexpr int NC = decltype(nc_c)::value;
     if (x_is_f32)
-      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<float, NC>), dim3(blocks), dim3(256), 0, s,
-                         static_cast<const float *>(x), shift, scale, static_cast<bf16 *>(h), T, D,
-                         (double)eps);
+      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<float, NC, OT>), dim3(blocks), dim3(256), 0,
+                         s, static_cast<const float *>(x), shift, scale, h, T, D, (double)eps);
     else
-      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<bf16, NC>), dim3(blocks), dim3(256), 0, s,
-                         static_cast<const bf16 *>(x), shift, scale, static_cast<bf16 *>(h), T, D,
-                         (double)eps);
+      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<bf16, NC, OT>), dim3(blocks), dim3(256), 0,
+                         s, static_cast<const bf16 *>(x), shift, scale, h, T, D, (double)eps);
     return hipGetLastError();
   };
   const int per_lane = (int)ceil_div(D, 64 * 8);  // 16-byte chunks per lane
@@ -157,14 +178,24 @@ hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *s
   if (per_lane <= 11) return reg(std::integral_constant<int, 11>());
   if (per_lane <= 16) return reg(std::integral_constant<int, 16>());
   if (x_is_f32)
-    hipLaunchKernelGGL(rmsnorm_modulate_kernel<float>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const float *>(x), shift, scale, static_cast<bf16 *>(h), T, D,
-                       (double)eps);
+    hipLaunchKernelGGL((rmsnorm_modulate_kernel<float, OT>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<const float *>(x), shift, scale, h, T, D, (double)eps);
   else
-    hipLaunchKernelGGL(rmsnorm_modulate_kernel<bf16>, dim3(blocks), dim3(256), 0, s,
-                       static_cast<const bf16 *>(x), shift, scale, static_cast<bf16 *>(h), T, D,
-                       (double)eps);
+    hipLaunchKernelGGL((rmsnorm_modulate_kernel<bf16, OT>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<const bf16 *>(x), shift, scale, h, T, D, (double)eps);
   return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *shift,
+                                   const double *scale, void *h, int T, int D, float eps,
+                                   hipStream_t s) {
+  return launch_rn(x, x_is_f32, shift, scale, static_cast<bf16 *>(h), T, D, eps, s);
+}
+
+hipError_t launch_rmsnorm_modulate_f32out(const void *x, bool x_is_f32, const double *shift,
+                                          const double *scale, float *h, int T, int D, float eps,
+                                          hipStream_t s) {
+  return launch_rn(x, x_is_f32, shift, scale, h, T, D, eps, s);
 }
 
 }  // namespace h3dit

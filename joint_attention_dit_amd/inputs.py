@@ -135,6 +135,92 @@ def make_inputs(cfg: BlockConfig, seed: int = 0) -> Dict[str, torch.Tensor]:
     return out
 
 
+# ---------------------------------------------------------------- DiT stack
+@dataclass(frozen=True)
+class StackConfig:
+    """The DiT around the blocks: n_blocks blocks of shape `block` (one target
+    image, text first), latents of `channels` channels cut into patch x patch
+    patches (one image token each), `steps` denoising steps."""
+    name: str
+    block: BlockConfig
+    n_blocks: int
+    channels: int
+    patch: int
+    steps: int
+    description: str = ""
+
+    @property
+    def grid(self) -> Tuple[int, int]:
+        rows, cols, _ = self.block.images[0]
+        return rows, cols
+
+    @property
+    def latent_shape(self) -> Tuple[int, int, int]:
+        rows, cols = self.grid
+        return self.channels, rows * self.patch, cols * self.patch
+
+    @property
+    def patch_features(self) -> int:
+        return self.channels * self.patch * self.patch
+
+
+STACK_CONFIGS: Dict[str, StackConfig] = {
+    "tiny_stack": StackConfig(
+        "tiny_stack",
+        block=small_config("tiny_stack", hidden=256, heads=2, ffn=1024, text_tokens=8,
+                           images=((4, 4, 0),)),
+        n_blocks=3, channels=4, patch=2, steps=2,
+        description="tiny DiT: 3 blocks of hidden 256, 4-channel 8x8 latent (4x4 tokens) + 8 text, 2 steps"),
+    "dit_2048": StackConfig(
+        "dit_2048", block=CONFIGS["2048"], n_blocks=50, channels=24, patch=2, steps=6,
+        description=("full DiT: 50 blocks, 6 denoising steps at 2048x2048 (24-channel 128x128 latent, "
+                     "64x64 image tokens + 256 text tokens)")),
+}
+
+
+def make_stack_inputs(scfg: StackConfig, seed: int = 0, device: str = "cpu",
+                      n_blocks: int = -1) -> Dict[str, object]:
+    """Seeded DiT-stack inputs. Draw order (one generator, `seed`): for every
+    block w_ada, w_qkv, w_o, w_up, w_down (bf16, N(0, 0.02^2)); then w_patch
+    (fp32 [D, C p p], N(0, 0.02^2)), w_ada_final (bf16 [2D, D]), w_final (fp32
+    [C p p, D], N(0, 0.02^2)), the latent (fp32, N(0, 1)) and the text tokens
+    (fp32 [text, D], N(0, 1)). Step k's cond vector (fp32 [D], N(0, 1)) comes
+    from its own generator seeded k. `device` "cuda" draws on the GPU (a
+    different stream of numbers than the CPU generator) for the full-size
+    stack; n_blocks < 0 means scfg.n_blocks."""
+    nb = scfg.n_blocks if n_blocks < 0 else n_blocks
+    b = scfg.block
+    D, A, F = b.hidden, b.attn_width, b.ffn
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def rnd(*shape, scale=1.0, dtype=torch.float32):
+        return (torch.randn(*shape, generator=g, dtype=torch.float32, device=device) * scale).to(dtype)
+
+    blocks = []
+    for _ in range(nb):
+        blocks.append({"w_ada": rnd(6 * D, D, scale=0.02, dtype=torch.bfloat16),
+                       "w_qkv": rnd(3 * A, D, scale=0.02, dtype=torch.bfloat16),
+                       "w_o": rnd(D, A, scale=0.02, dtype=torch.bfloat16),
+                       "w_up": rnd(F, D, scale=0.02, dtype=torch.bfloat16),
+                       "w_down": rnd(D, F, scale=0.02, dtype=torch.bfloat16)})
+    P = scfg.patch_features
+    out: Dict[str, object] = {"blocks": blocks}
+    out["w_patch"] = rnd(D, P, scale=0.02)
+    out["w_ada_final"] = rnd(2 * D, D, scale=0.02, dtype=torch.bfloat16)
+    out["w_final"] = rnd(P, D, scale=0.02)
+    out["latent"] = rnd(*scfg.latent_shape)
+    out["text"] = rnd(b.text_tokens, D)
+    conds = []
+    for k in range(scfg.steps):
+        gk = torch.Generator(device=device)
+        gk.manual_seed(k)
+        conds.append(torch.randn(D, generator=gk, dtype=torch.float32, device=device))
+    out["conds"] = conds
+    out["positions"] = torch.from_numpy(positions(b)).to(device)
+    return out
+
+
 def sample_rows(n_tokens: int, n: int = 256, seed: int = 1) -> np.ndarray:
     """Sorted token indices for sampled-row parity; all rows when n >= T."""
     if n >= n_tokens:

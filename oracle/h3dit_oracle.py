@@ -231,3 +231,57 @@ def block_forward(x: np.ndarray, cond: np.ndarray, w: Dict[str, np.ndarray], pos
 
     return dict(mod=mod, h1=h1, q=q.reshape(len(r), A), k=k.reshape(T, A), v=v.reshape(T, A),
                 o=o, x1=x1, h2=h2, u=u, out=out, rows=r)
+
+
+# ----------------------------------------------------------------------------
+# the DiT around the blocks (model card, "Model Architecture": latent patches
+# become the image tokens of the packed sequence; spec page,
+# "Specifications": 50 layers). Readings where the pages are silent: the
+# patch embedding and the final projection are plain fp32 linears without
+# bias; the final layer is a modulated RMSNorm (shift, scale from its own
+# AdaLN linear of cond) followed by the projection, like the blocks' norms;
+# the same cond feeds every block of one evaluation.
+# ----------------------------------------------------------------------------
+def patchify(latent: np.ndarray, p: int) -> np.ndarray:
+    """latent [C, H, W] -> patches [(H/p)(W/p), C p p]; token t = gy (W/p) + gx,
+    feature c p p + dy p + dx holds latent[c, gy p + dy, gx p + dx]."""
+    C, H, W = latent.shape
+    gh, gw = H // p, W // p
+    return latent.reshape(C, gh, p, gw, p).transpose(1, 3, 0, 2, 4).reshape(gh * gw, C * p * p)
+
+
+def unpatchify(vt: np.ndarray, C: int, p: int, gh: int, gw: int) -> np.ndarray:
+    """Inverse of patchify: per-token rows [gh gw, C p p] -> [C, gh p, gw p]."""
+    return vt.reshape(gh, gw, C, p, p).transpose(2, 0, 3, 1, 4).reshape(C, gh * p, gw * p)
+
+
+def final_layer(x_img: np.ndarray, cond: np.ndarray, w_ada_final: np.ndarray,
+                w_final: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """(rmsnorm(x) * (1 + scale) + shift) . w_final^T with (shift, scale) = w_ada_final . cond."""
+    D = x_img.shape[1]
+    mod = w_ada_final @ cond
+    shift, scale = mod[:D], mod[D:2 * D]
+    return (rms_normalize(x_img, eps) * (1.0 + scale) + shift) @ w_final.T
+
+
+def dit_forward(latent: np.ndarray, text: np.ndarray, cond: np.ndarray, w_patch: np.ndarray,
+                w_ada_final: np.ndarray, w_final: np.ndarray, blocks, pos: np.ndarray,
+                heads: int, patch: int, eps: float = 1e-6, rope_base: float = 10000.0,
+                mode: str = "contract") -> np.ndarray:
+    """One DiT evaluation: v [C, H, W] for latent [C, H, W] (see module notes)."""
+    C, H, W = latent.shape
+    x = np.concatenate([text, patchify(latent, patch) @ w_patch.T], axis=0)
+    for w in blocks:
+        x = block_forward(x, cond, w, pos, heads=heads, eps=eps, rope_base=rope_base,
+                          mode=mode)["out"]
+    vt = final_layer(x[text.shape[0]:], cond, w_ada_final, w_final, eps)
+    return unpatchify(vt, C, patch, H // patch, W // patch)
+
+
+def euler_sample(latent: np.ndarray, conds, dt: float, **dit_kwargs) -> np.ndarray:
+    """Explicit Euler steps latent <- latent + dt * v(latent, cond_k), one per cond.
+    The pages do not give the sampler's schedule; this fixed-step update is a
+    stand-in that exercises the repeated evaluation, not the model's sampler."""
+    for cond in conds:
+        latent = latent + dt * dit_forward(latent, cond=cond, **dit_kwargs)
+    return latent

@@ -135,3 +135,64 @@ def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5):
         assert lib.h3dit_status_string(s).startswith(b"H3DIT_")
     assert b"unknown" in lib.h3dit_status_string(42)
+
+
+# ---------------------------------------------------------------- DiT stack
+def stack_cfg(n_blocks=2, text=256, grid=64):
+    return B.StackConfig(n_blocks, 24, 2, grid, grid, text)
+
+
+def test_stack_struct_layout_and_workspace():
+    assert ctypes.sizeof(B.StackConfig) == 24
+    assert ctypes.sizeof(B.StackWeights) == 32
+    cfg = B.make_config(5376, 56, 14336, 4352, B.H3DIT_F32)
+    n = B.h3dit_stack_workspace_size(cfg, stack_cfg())
+    T, D, Ti, F = 4352, 5376, 4096, 96
+    extra = 2 * 4 * T * D + 4 * Ti * F + 16 * D + 4 * Ti * D + 4 * Ti * F
+    blk = B.h3dit_workspace_size(cfg)
+    assert blk + extra <= n <= blk + extra + 8 * 256
+
+
+def test_stack_shape_validation():
+    cfg = B.make_config(256, 2, 1024, 24)
+    with pytest.raises(B.H3ditError) as ei:     # 8 text + 5 x 4 image tokens != 24
+        B.h3dit_stack_workspace_size(cfg, B.StackConfig(1, 4, 2, 5, 4, 8))
+    assert ei.value.status == B.H3DIT_EINVAL
+    with pytest.raises(B.H3ditError) as ei:     # 3 features per patch (not a multiple of 4)
+        B.h3dit_stack_workspace_size(cfg, B.StackConfig(1, 3, 1, 4, 4, 8))
+    assert ei.value.status == B.H3DIT_EUNSUPPORTED
+    with pytest.raises(B.H3ditError) as ei:
+        B.h3dit_stack_workspace_size(cfg, B.StackConfig(-1, 4, 2, 4, 4, 8))
+    assert ei.value.status == B.H3DIT_EINVAL
+
+
+def _dit(lib, cfg, st, ws_bytes=1 << 40, blocks=2, **override):
+    p = {k: 0x100000000 * (i + 1) for i, k in enumerate(
+        ["latent", "text", "cond", "pos", "v", "ws", "wp", "wa", "wf"])}
+    p.update(override)
+    arr = (B.Weights * blocks)(*[B.Weights(*[0x20000000000 + 0x1000000000 * (5 * b + j)
+                                             for j in range(5)]) for b in range(blocks)])
+    sw = B.StackWeights(p["wp"], p["wa"], p["wf"], ctypes.cast(arr, ctypes.POINTER(B.Weights)))
+    return lib.h3dit_dit_forward(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), p["latent"],
+                                 p["text"], p["cond"], p["pos"], p["v"], p["ws"], ws_bytes, None)
+
+
+def test_dit_forward_validation(lib):
+    cfg = B.make_config(5376, 56, 14336, 4352, B.H3DIT_F32)
+    st = stack_cfg()
+    assert _dit(lib, cfg, st, latent=None) == B.H3DIT_EINVAL
+    assert _dit(lib, cfg, st, wf=0x100000004) == B.H3DIT_EALIGN
+    assert _dit(lib, cfg, st, ws_bytes=4096) == B.H3DIT_EWORKSPACE
+    assert _dit(lib, cfg, st, v=0x100000000 * 6 + 64) == B.H3DIT_EINVAL      # inside the workspace
+    assert "overlaps" in lib.h3dit_last_error().decode()
+    bad = B.StackWeights(0x100000000 * 7, 0x100000000 * 8, 0x100000000 * 9, None)
+    assert lib.h3dit_dit_forward(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(bad),
+                                 0x100000000, 0x200000000, 0x300000000, 0x400000000, 0x500000000,
+                                 0x600000000, 1 << 40, None) == B.H3DIT_EINVAL
+    assert "blocks is NULL" in lib.h3dit_last_error().decode()
+
+
+def test_latent_step_validation(lib):
+    assert lib.h3dit_latent_step(None, 0x100000000, 0.5, 10, None) == B.H3DIT_EINVAL
+    assert lib.h3dit_latent_step(0x100000000, 0x200000000, 0.5, 0, None) == B.H3DIT_EINVAL
+    assert lib.h3dit_latent_step(0x100000000, 0x200000000, float("nan"), 4, None) == B.H3DIT_EINVAL
