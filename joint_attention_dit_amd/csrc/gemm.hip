@@ -4,29 +4,35 @@
 //
 //   C[t, n] = sum_k X[t, k] * W[n, k]      X: activations [M, K], W: weights [N, K]
 //
-// Both operands are K-contiguous, so both feed the 32x32x16 bf16 MFMA
+// Both operands are K-contiguous, so both feed the 16x16x32 bf16 MFMA
 // directly. The weight rows are the MFMA "A" rows and the token rows the
 // "B" columns, which leaves every lane holding four consecutive output
 // features of one token: RoPE pairs (2i, 2i+1) sit in one lane and stores are
 // 8- or 16-byte vectors.
 //
-// Tiling: 256 features x 256 tokens per workgroup, K step 64 (four MFMA
-// k-steps of 16), eight waves (two per SIMD) in a 2 x 4 arrangement, each
-// owning 128 features x 64 tokens (4 x 2 blocks of 32 x 32, 128 fp32
-// accumulators per lane). With two waves per SIMD one wave's matrix cores
-// keep running while the other waits at the barrier or issues its copies.
-// Global tiles go straight into LDS (gfx950's 16-byte global-load-to-LDS),
-// double buffered, 64 KB per stage. Every tile row is one 128-byte segment of
-// a K-contiguous matrix row: copies of 64-byte segments reach only about half
-// the global-to-LDS rate per CU that this tile needs. The fragments of each
-// k-step are read from LDS while the previous k-step's MFMAs run. One barrier
-// per K step, after the first MFMAs of the last k-step: by then every wave has
-// read its last fragments of the current stage (so the stage can take the
-// tile after next) and the next tile has landed (so its first fragments are
-// read during the last k-step). The copies of a tile are spread over the MFMA
-// groups of two k-steps instead of issued in one burst. LDS rows are 128
-// bytes; 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), so
-// the 16 rows read by a quarter-wave fragment load cover all 64 banks.
+// Tiling: 256 features x 256 tokens per workgroup, K step 64 (two MFMA
+// k-steps of 32), eight waves (two per SIMD) in a 2 x 4 arrangement, each
+// owning 128 features x 64 tokens (8 x 4 blocks of 16 x 16, 128 fp32
+// accumulators per lane). The 16x16x32 product is used rather than 32x32x16:
+// on random operands the chip runs into its power limit, and the smaller
+// product (half the accumulator traffic per flop) sustains about a quarter
+// more throughput there. With two waves per SIMD one wave's matrix cores keep
+// running while the other waits at the barrier or issues its copies.
+// Global tiles go straight into LDS (gfx950's 16-byte global-load-to-LDS).
+// Every tile row is one 128-byte segment of a K-contiguous matrix row: copies
+// of 64-byte segments reach only about half the global-to-LDS rate per CU that
+// this tile needs. The weight tile has two LDS stages and the activation tile
+// three (5 x 32 KB = 160 KB): activation panels are shared by fewer concurrent
+// workgroups than weight panels, miss L2 more often and so get copies issued
+// two K steps ahead instead of one. One barrier per K step, after the first
+// products of the second k-step: by then every wave has read its last
+// fragments of the current tile (so its stages take weight tile kt + 2 and
+// activation tile kt + 3, copied right after the barrier) and the next tile
+// has landed (so its first fragments are read during the second k-step). A
+// fragments are re-read in place as soon as their four products have issued,
+// B fragments are double buffered. LDS rows are 128 bytes; 16-byte chunk c of
+// row r is stored at chunk c ^ ((r >> 1) & 7), so the 16 rows read by a
+// quarter-wave fragment load cover all 64 banks.
 //
 // Workgroup order: the dispatcher hands workgroup i to XCD i % 8. The
 // linear id is remapped so that each XCD receives a contiguous range of
@@ -44,7 +50,6 @@ namespace {
 constexpr int BN = 256;   // weight rows (output features) per tile
 constexpr int BT = 256;   // activation rows (tokens) per tile
 constexpr int BK = 64;    // K per LDS stage (128-byte rows)
-constexpr int NSTAGE = 2; // LDS stages
 constexpr int TILE_ELEMS = 256 * BK;  // one operand tile, bf16 elements (32 KB)
 constexpr int GROUP_T = 8;
 
@@ -141,11 +146,13 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
 
 // Wait until at most N of this wave's global-to-LDS copies are still in
 // flight (they complete in issue order), then meet the other waves: afterwards
-// every wave's earlier copies have landed in LDS.
+// every wave's earlier copies have landed in LDS. Instructions are not moved
+// across it in either direction.
 template <int N>
 __device__ __forceinline__ void tile_barrier() {
   // s_waitcnt vmcnt(N) (lgkmcnt and expcnt fields left at their maximum)
   constexpr int enc = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(enc);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -153,7 +160,8 @@ __device__ __forceinline__ void tile_barrier() {
 
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) bf16 lds[NSTAGE * 2 * TILE_ELEMS];  // 128 KB
+  // weight tiles: 2 stages of 32 KB; activation tiles: 3 stages of 32 KB (160 KB)
+  __shared__ __attribute__((aligned(1024))) bf16 lds[5 * TILE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -179,147 +187,150 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
     xoff[j] = (uint32_t)(min(t0 + row, a.M - 1) - t0) * (uint32_t)a.K * 2u + lc * 16u;
   }
   const uint32_t lds0 = lds_address(lds);
-  // copies j0 .. j1-1 of each operand of the tile at k0 into stage
-  auto dload_part = [&](int stage, int k0, int j0, int j1) {
+  // copies j0 .. j1-1 of the weight (activation) tile at k0 into weight stage
+  // wst (activation stage xst)
+  auto wload = [&](int wst, int k0, int j0, int j1) {
     const char *wp = wpanel + (int64_t)k0 * 2;
-    const char *xp = xpanel + (int64_t)k0 * 2;
-    const uint32_t sw = lds0 + (uint32_t)(stage * 2 * TILE_ELEMS + wave * 4 * 512) * 2u;
-    const uint32_t sx = sw + TILE_ELEMS * 2;
+    const uint32_t sw = lds0 + (uint32_t)(wst * TILE_ELEMS + wave * 4 * 512) * 2u;
 #pragma unroll
-    for (int j = j0; j < j1; ++j) {
-      dma16(wp, woff[j], sw + j * 1024);
-      dma16(xp, xoff[j], sx + j * 1024);
-    }
+    for (int j = j0; j < j1; ++j) dma16(wp, woff[j], sw + j * 1024);
+  };
+  auto xload = [&](int xst, int k0, int j0, int j1) {
+    const char *xp = xpanel + (int64_t)k0 * 2;
+    const uint32_t sx = lds0 + (uint32_t)((2 + xst) * TILE_ELEMS + wave * 4 * 512) * 2u;
+#pragma unroll
+    for (int j = j0; j < j1; ++j) dma16(xp, xoff[j], sx + j * 1024);
   };
 
-  // fragment reads: lane row r32 of each 32-row block, k chunk 2 s + kh of the K
-  // tile (k-step s of 16); the swizzle depends on r32 only, so block b sits at a
-  // fixed offset of b * 32 rows
-  const int r32 = lane & 31, kh = lane >> 5;
-  int fa_base[4], fb_base[4];
+  // fragment reads: lane row r16 of each 16-row block, k chunk 4 s + kq of the
+  // K tile (k-step s of 32); the swizzle depends on r16 only, so block b sits at
+  // a fixed offset of b * 16 rows
+  const int r16 = lane & 15, kq = lane >> 4;
+  int fa_base[2], fb_base[2];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    fa_base[s] = (wn * 128 + r32) * BK + (swz(r32, 2 * s + kh) * 8);
-    fb_base[s] = (wt * 64 + r32) * BK + (swz(r32, 2 * s + kh) * 8);
+  for (int s = 0; s < 2; ++s) {
+    fa_base[s] = (wn * 128 + r16) * BK + (swz(r16, 4 * s + kq) * 8);
+    fb_base[s] = (wt * 64 + r16) * BK + (swz(r16, 4 * s + kq) * 8);
   }
 
-  f32x16 acc[4][2];
+  f32x4 acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
 
   const int ktiles = a.K / BK;
 
-  bf16x8 fa[2][4], fb[2][2];
-  auto fload_all = [&](int stage, int s, int buf) {
-    const bf16 *sw = lds + stage * 2 * TILE_ELEMS;
-    const bf16 *sx = sw + TILE_ELEMS;
+  // A fragments are re-read in place once their four products have issued; B
+  // fragments are double buffered
+  bf16x8 fa[8], fb[2][4];
+  auto fload_all = [&](int wst, int xst, int s, int buf) {
+    const bf16 *sw = lds + wst * TILE_ELEMS;
+    const bf16 *sx = lds + (2 + xst) * TILE_ELEMS;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      fb[buf][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[s] + j * 32 * BK);
+    for (int j = 0; j < 4; ++j)
+      fb[buf][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[s] + j * 16 * BK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fa[buf][i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[s] + i * 32 * BK);
+    for (int i = 0; i < 8; ++i)
+      fa[i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[s] + i * 16 * BK);
   };
-  // One k-step of 8 MFMAs on buffer BCUR; the fragments of k-step ns of LDS
-  // stage nstage are fetched into the other buffer meanwhile. When SYNC, the
-  // wave meets the others after its first 2 MFMAs (the next tile has then
-  // landed everywhere and nobody reads this tile's stage again). DMA selects
-  // the copies issued between the MFMA groups: 1 = the first half of tile
-  // kt + 2 into this tile's stage (after the barrier), 2 = the second half of
-  // tile kt + 1 (begun in the previous K step). With RT the copies are issued
-  // only when the runtime flag dma_on is set.
-  auto kstep = [&](auto bcur_c, auto sync_c, auto dma_c, auto rt_c, bool dma_on, int nstage,
-                   int ns, int kt) {
-    constexpr int BCUR = decltype(bcur_c)::value, DMA = decltype(dma_c)::value;
+  // One k-step (32 of K) of 32 products on B buffer BCUR; the fragments of
+  // k-step ns of weight stage wst_n and activation stage xst_n are fetched
+  // meanwhile. When SYNC, the wave first settles its fragment reads, then
+  // meets the others after its first 4 products (waiting for its own copies of
+  // tile kt + 1; with vm4 the last four copies, activation tile kt + 2, may
+  // still be in flight) and afterwards issues the copies of weight tile kt + 2
+  // (wref) and activation tile kt + 3 (xref). With RT the three flags are
+  // taken at run time, otherwise all of them hold.
+  auto kstep = [&](auto bcur_c, auto sync_c, auto rt_c, bool wref, bool xref, bool vm4, int wst_n,
+                   int xst_n, int ns, int kt, int xs) {
+    constexpr int BCUR = decltype(bcur_c)::value;
     constexpr bool SYNC = decltype(sync_c)::value, RT = decltype(rt_c)::value;
-    const bf16 *sw = lds + nstage * 2 * TILE_ELEMS;
-    const bf16 *sx = sw + TILE_ELEMS;
+    const bf16 *sw = lds + wst_n * TILE_ELEMS;
+    const bf16 *sx = lds + (2 + xst_n) * TILE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[BCUR][i], fb[BCUR][j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i], fb[BCUR][j], acc[i][j]);
       if constexpr (SYNC) {
-        if (i == 0) tile_barrier<0>();
-      }
-      if (!RT || dma_on) {
-        if constexpr (DMA == 1) {
-          if (i == 1) dload_part(kt & 1, (kt + 2) * BK, 0, 1);
-          if (i == 2) dload_part(kt & 1, (kt + 2) * BK, 1, 2);
+        if (i == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));
+          if (!RT || vm4) tile_barrier<4>();
+          else tile_barrier<0>();
         }
-        if constexpr (DMA == 2) {
-          if (i == 0) dload_part((kt + 1) & 1, (kt + 1) * BK, 2, 3);
-          if (i == 2) dload_part((kt + 1) & 1, (kt + 1) * BK, 3, 4);
-        }
+        if (i == 1 && (!RT || wref)) wload(kt & 1, (kt + 2) * BK, 0, 2);
+        if (i == 2 && (!RT || wref)) wload(kt & 1, (kt + 2) * BK, 2, 4);
+        if (i == 3 && (!RT || xref)) xload(xs, (kt + 3) * BK, 0, 2);
+        if (i == 4 && (!RT || xref)) xload(xs, (kt + 3) * BK, 2, 4);
       }
       if (i == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          fb[BCUR ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + j * 32 * BK);
+        for (int j = 0; j < 4; ++j)
+          fb[BCUR ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + j * 16 * BK);
       }
-      if (i == 1) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          fa[BCUR ^ 1][r] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + r * 32 * BK);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (i == 1) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      fa[i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + i * 16 * BK);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using D0 = std::integral_constant<int, 0>;
-  using D1 = std::integral_constant<int, 1>;
-  using D2 = std::integral_constant<int, 2>;
   using Y = std::true_type;
   using N = std::false_type;
 
-  // One K step over the tile in stage kt & 1: k-steps 0..3, the last one with
-  // the barrier and the first fragments of tile kt + 1. Tile kt + 2 is copied
-  // into this stage in two halves: during k-step 3 (after the barrier) and
-  // during k-step 0 of the next K step. In the steady state every copy is
-  // present (RT false); the first and last K steps decide at run time. The
-  // last K step still reads (stale) fragments of the other stage and meets
-  // the other waves once more, which is harmless.
-  auto ktile = [&](auto rt_c, int kt) {
-    const bool tail = kt >= 1 && kt + 1 < ktiles;
-    const bool refill = kt + 2 < ktiles;
-    const int st = kt & 1;
-    kstep(I0(), N(), D2(), rt_c, tail, st, 1, kt);
-    kstep(I1(), N(), D0(), rt_c, false, st, 2, kt);
-    kstep(I0(), N(), D0(), rt_c, false, st, 3, kt);
-    kstep(I1(), Y(), D1(), rt_c, refill, st ^ 1, 0, kt);
+  // K step kt: weight tile kt in stage kt & 1, activation tile kt in stage
+  // xs = kt % 3. The copies of each K step are issued in the order weight tile
+  // kt + 2, activation tile kt + 3, so at the barrier of K step kt + 1 exactly
+  // the four copies of activation tile kt + 3 are younger than everything tile
+  // kt + 2 needs. The last K step still reads (stale) fragments of the next
+  // stages and meets the other waves once more, which is harmless.
+  auto ktile = [&](auto rt_c, int kt, int xs) {
+    const int xn = xs == 2 ? 0 : xs + 1;
+    kstep(I0(), N(), rt_c, false, false, false, kt & 1, xs, 1, kt, xs);
+    kstep(I1(), Y(), rt_c, kt + 2 < ktiles, kt + 3 < ktiles, kt + 2 < ktiles, (kt + 1) & 1, xn, 0,
+          kt, xs);
   };
 
-  dload_part(0, 0, 0, 4);
+  wload(0, 0, 0, 4);
+  xload(0, 0, 0, 4);
   if (ktiles > 1) {
-    dload_part(1, BK, 0, 4);
+    wload(1, BK, 0, 4);
+    xload(1, BK, 0, 4);
+  }
+  if (ktiles > 2) {
+    xload(2, 2 * BK, 0, 4);
+    tile_barrier<12>();
+  } else if (ktiles > 1) {
     tile_barrier<8>();
   } else {
     tile_barrier<0>();
   }
-  fload_all(0, 0, 0);
+  fload_all(0, 0, 0, 0);
   // settle the scalar loads once (pending ones would make the compiler wait for
   // all LDS reads at each k-step); copies stay in flight
   __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
-  ktile(Y(), 0);
-  int kt = 1;
-  for (; kt + 2 < ktiles; ++kt) ktile(N(), kt);
-  for (; kt < ktiles; ++kt) ktile(Y(), kt);
+  ktile(Y(), 0, 0);
+  int kt = 1, xs = 1;
+  for (; kt + 3 < ktiles; ++kt) {
+    ktile(N(), kt, xs);
+    xs = xs == 2 ? 0 : xs + 1;
+  }
+  for (; kt < ktiles; ++kt) {
+    ktile(Y(), kt, xs);
+    xs = xs == 2 ? 0 : xs + 1;
+  }
 
-  const int nb = n0 + wn * 128 + 4 * kh, tb = t0 + wt * 64 + r32;
+  const int nb = n0 + wn * 128 + 4 * kq, tb = t0 + wt * 64 + r16;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store4<EPI>(a, tb + 32 * j, nb + 32 * i + 8 * g, acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                    acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+    for (int i = 0; i < 8; ++i)
+      store4<EPI>(a, tb + 16 * j, nb + 16 * i, acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                  acc[i][j][3]);
 }
 
 }  // namespace
