@@ -41,6 +41,7 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace h3dit {
@@ -57,13 +58,9 @@ constexpr int GROUP_T = 8;
 // so chunk c of row r is stored at chunk c ^ ((r >> 1) & 7).
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_n, int tiles_t,
-                                            int &tn, int &tt) {
-  // XCD-contiguous remap (bijective for any nblocks)
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int q = nblocks >> 3, r = nblocks & 7;
-  const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
-  // grouped walk: GROUP_T token tiles per group, features outer within the group
+// Tile L of the grouped walk: GROUP_T token tiles per group, features outer
+// within the group.
+__device__ __forceinline__ void walk_coords(int L, int tiles_n, int tiles_t, int &tn, int &tt) {
   const int per_group = GROUP_T * tiles_n;
   const int g = L / per_group;
   const int first_t = g * GROUP_T;
@@ -71,6 +68,21 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_n, i
   const int in = L - g * per_group;
   tt = first_t + in % gt;
   tn = in / gt;
+}
+
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_n, int tiles_t,
+                                            int &tn, int &tt) {
+  // XCD-contiguous remap (bijective for any nblocks)
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+  walk_coords(L, tiles_n, tiles_t, tn, tt);
+}
+
+// Split tiles: K slices of one tile are workgroups full_tiles + t * split + s;
+// slice s covers K tiles [s * per, min((s + 1) * per, ktiles)).
+__device__ __forceinline__ int slice_ktiles(int ktiles, int split) {
+  return (ktiles + split - 1) / split;
 }
 
 __device__ __forceinline__ float gelu_tanh(float z) {
@@ -168,16 +180,27 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wt = wave >> 1;  // 2 x 4 waves of 128 features x 64 tokens
   const int tiles_n = (int)ceil_div(a.N, BN), tiles_t = (int)ceil_div(a.M, BT);
-  int tn, tt;
-  tile_coords(blockIdx.x, gridDim.x, tiles_n, tiles_t, tn, tt);
+  // whole tile, or K slice `piece` of one of the split tiles of the last wave
+  int tn, tt, piece = -1, kb0 = 0, ktiles = a.K / BK;
+  if (a.split <= 1) {
+    tile_coords(blockIdx.x, gridDim.x, tiles_n, tiles_t, tn, tt);
+  } else if ((int)blockIdx.x < a.full_tiles) {
+    tile_coords(blockIdx.x, a.full_tiles, tiles_n, tiles_t, tn, tt);
+  } else {
+    piece = (int)blockIdx.x - a.full_tiles;
+    walk_coords(a.full_tiles + piece / a.split, tiles_n, tiles_t, tn, tt);
+    const int per = slice_ktiles(ktiles, a.split);
+    kb0 = (piece % a.split) * per;
+    ktiles = min(per, ktiles - kb0);
+  }
   const int n0 = tn * BN, t0 = tt * BT;
 
   // global -> LDS without registers: each wave fills 4 blocks of 1 KB (8 rows of
   // 128 bytes) per operand tile; lane l lands at byte 16 l of its block, i.e. at
   // row 8 b + l / 8, physical chunk l % 8, so it fetches logical chunk
   // (l % 8) ^ swz(row). Rows past the matrix edge repeat the last row.
-  const char *wpanel = static_cast<const char *>(a.w) + (int64_t)n0 * a.K * 2;
-  const char *xpanel = static_cast<const char *>(a.x) + (int64_t)t0 * a.K * 2;
+  const char *wpanel = static_cast<const char *>(a.w) + ((int64_t)n0 * a.K + kb0 * BK) * 2;
+  const char *xpanel = static_cast<const char *>(a.x) + ((int64_t)t0 * a.K + kb0 * BK) * 2;
   uint32_t woff[4], xoff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -220,8 +243,6 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
-
-  const int ktiles = a.K / BK;
 
   // A fragments are re-read in place once their four products have issued; B
   // fragments are double buffered
@@ -324,6 +345,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
     xs = xs == 2 ? 0 : xs + 1;
   }
 
+  if (piece >= 0) {  // a K slice: raw sums to the scratch, [register block][thread]
+    f32x4 *dst = reinterpret_cast<f32x4 *>(a.partial) + (int64_t)piece * (32 * 512) + tid;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[(i * 4 + j) * 512] = acc[i][j];
+    return;
+  }
   const int nb = n0 + wn * 128 + 4 * kq, tb = t0 + wt * 64 + r16;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -333,28 +362,96 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
                   acc[i][j][3]);
 }
 
+// Sum of the K slices of split tile full_tiles + blockIdx.x (in slice order),
+// then the epilogue, with the thread -> output mapping of gemm_kernel.
+template <int EPI>
+__global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 1, wt = wave >> 1;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int tiles_n = (int)ceil_div(a.N, BN), tiles_t = (int)ceil_div(a.M, BT);
+  int tn, tt;
+  walk_coords(a.full_tiles + blockIdx.x, tiles_n, tiles_t, tn, tt);
+  const f32x4 *src =
+      reinterpret_cast<const f32x4 *>(a.partial) + (int64_t)blockIdx.x * a.split * (32 * 512) + tid;
+  const int nb = tn * BN + wn * 128 + 4 * kq, tb = tt * BT + wt * 64 + r16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t o = (i * 4 + j) * 512;
+      f32x4 v = src[o];
+      for (int sl = 1; sl < a.split; ++sl) v += src[(int64_t)sl * (32 * 512) + o];
+      store4<EPI>(a, tb + 16 * j, nb + 16 * i, v[0], v[1], v[2], v[3]);
+    }
+}
+
 }  // namespace
 
-hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s) {
-  const int tiles = (int)(ceil_div(a.N, BN) * ceil_div(a.M, BT));
-  switch (epi) {
-    case EPI_QKV_ROPE:
-      hipLaunchKernelGGL(gemm_kernel<EPI_QKV_ROPE>, dim3(tiles), dim3(512), 0, s, a);
-      break;
-    case EPI_RESID_BF16:
-      hipLaunchKernelGGL(gemm_kernel<EPI_RESID_BF16>, dim3(tiles), dim3(512), 0, s, a);
-      break;
-    case EPI_RESID_F32:
-      hipLaunchKernelGGL(gemm_kernel<EPI_RESID_F32>, dim3(tiles), dim3(512), 0, s, a);
-      break;
-    case EPI_GELU:
-      hipLaunchKernelGGL(gemm_kernel<EPI_GELU>, dim3(tiles), dim3(512), 0, s, a);
-      break;
-    case EPI_F32:
-      hipLaunchKernelGGL(gemm_kernel<EPI_F32>, dim3(tiles), dim3(512), 0, s, a);
-      break;
+// Compute units of the current device (cached per device).
+constexpr int kPlanCus = 256;  // MI355X; scratch is sized for it, larger devices split less
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cached[dev] = n;
   }
+  return cached[dev];
+}
+
+// One workgroup per CU at a time: when the last wave of tiles is at most half
+// full, its tiles are split along K into as many slices as fill the CUs (and
+// fit the scratch); a second kernel adds the slices. Returns the number of
+// slices per split tile (1: no split) and the number of split tiles.
+static int plan_split(int64_t M, int64_t N, int64_t K, int cus, size_t scratch_bytes, int *rem_out) {
+  const int tiles = (int)(ceil_div(N, BN) * ceil_div(M, BT));
+  const int ktiles = (int)(K / BK);
+  const int rem = tiles % cus;
+  *rem_out = 0;
+  if (rem == 0 || 2 * rem > cus || ktiles < 2) return 1;
+  const size_t piece_bytes = (size_t)BN * BT * 4;
+  const size_t fit = scratch_bytes / (piece_bytes * (size_t)rem);
+  const int split = (int)std::min<size_t>((size_t)std::min(cus / rem, ktiles), fit);
+  if (split < 2) return 1;
+  const int per = (ktiles + split - 1) / split;
+  *rem_out = rem;
+  return (ktiles + per - 1) / per;  // every slice non-empty
+}
+
+size_t gemm_split_scratch_bytes(int64_t M, int64_t N, int64_t K) {
+  int rem = 0;
+  const int split = plan_split(M, N, K, kPlanCus, (size_t)-1, &rem);
+  return split > 1 ? (size_t)rem * split * BN * BT * 4 : 0;
+}
+
+template <int EPI>
+static hipError_t launch_epi(const GemmArgs &a0, hipStream_t s) {
+  GemmArgs a = a0;
+  const int tiles = (int)(ceil_div(a.N, BN) * ceil_div(a.M, BT));
+  int rem = 0;
+  a.split = a.partial ? plan_split(a.M, a.N, a.K, device_cus(), a.partial_bytes, &rem) : 1;
+  a.full_tiles = tiles - (a.split > 1 ? rem : 0);
+  const int grid = a.split > 1 ? a.full_tiles + rem * a.split : tiles;
+  hipLaunchKernelGGL(gemm_kernel<EPI>, dim3(grid), dim3(512), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.split <= 1) return e;
+  hipLaunchKernelGGL(gemm_fixup_kernel<EPI>, dim3(rem), dim3(512), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s) {
+  switch (epi) {
+    case EPI_QKV_ROPE: return launch_epi<EPI_QKV_ROPE>(a, s);
+    case EPI_RESID_BF16: return launch_epi<EPI_RESID_BF16>(a, s);
+    case EPI_RESID_F32: return launch_epi<EPI_RESID_F32>(a, s);
+    case EPI_GELU: return launch_epi<EPI_GELU>(a, s);
+    case EPI_F32: return launch_epi<EPI_F32>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace h3dit

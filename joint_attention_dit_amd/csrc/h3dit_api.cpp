@@ -4,6 +4,7 @@
 // modulation, RMSNorm, GELU MLP, residual).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -89,7 +90,7 @@ int check_config(const h3dit_config *cfg) {
 
 struct Plan {
   int64_t T, D, A, H, F, Tp;
-  size_t mod, table, h, qk, vt, o, x1, u, total;
+  size_t mod, table, h, qk, vt, o, x1, u, split, split_bytes, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -116,6 +117,12 @@ Plan make_plan(const h3dit_config *c) {
   p.o = take(2 * p.T * p.A);
   p.x1 = take(4 * p.T * p.D);
   p.u = take(2 * p.T * p.F);
+  // K slices of the four GEMMs' last waves (one GEMM at a time)
+  p.split_bytes = std::max(std::max(gemm_split_scratch_bytes(p.T, 3 * p.A, p.D),
+                                    gemm_split_scratch_bytes(p.T, p.D, p.A)),
+                           std::max(gemm_split_scratch_bytes(p.T, p.F, p.D),
+                                    gemm_split_scratch_bytes(p.T, p.D, p.F)));
+  p.split = take(p.split_bytes);
   p.total = off;
   return p;
 }
@@ -178,6 +185,7 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   float *x1 = at<float>(ws, p.x1);
   void *u = at<void>(ws, p.u);
   const int T = (int)p.T, D = (int)p.D, A = (int)p.A, F = (int)p.F, H = (int)p.H;
+  float *split = at<float>(ws, p.split);
 
   auto mark = [&](int i) -> hipError_t {
     if (!events) return hipSuccess;
@@ -200,6 +208,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.table = table;
     g.A = A;
     g.Mp = (int)p.Tp;
+    g.partial = split;
+    g.partial_bytes = p.split_bytes;
     LAUNCH(launch_gemm(EPI_QKV_ROPE, g, s), "qkv gemm");
   }
   LAUNCH(mark(4), "event record");
@@ -210,6 +220,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.out = x1;
     g.resid = x;
     g.gate = mod + 2 * D;
+    g.partial = split;
+    g.partial_bytes = p.split_bytes;
     LAUNCH(launch_gemm(cfg->x_dtype == H3DIT_F32 ? EPI_RESID_F32 : EPI_RESID_BF16, g, s),
            "output projection");
   }
@@ -220,6 +232,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   {
     GemmArgs g = gemm_args(h, w->w_up, T, F, D);
     g.out = u;
+    g.partial = split;
+    g.partial_bytes = p.split_bytes;
     LAUNCH(launch_gemm(EPI_GELU, g, s), "mlp up");
   }
   LAUNCH(mark(8), "event record");
@@ -228,6 +242,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.out = out;
     g.resid = x1;
     g.gate = mod + 5 * D;
+    g.partial = split;
+    g.partial_bytes = p.split_bytes;
     LAUNCH(launch_gemm(EPI_RESID_F32, g, s), "mlp down");
   }
   LAUNCH(mark(9), "event record");

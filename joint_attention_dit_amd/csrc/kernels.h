@@ -38,9 +38,22 @@ struct GemmArgs {
   const float *table; // QKV: rope table [M, 64] float2
   int A;              // QKV: attention width
   int Mp;             // QKV: padded token count of vt
+  // Optional scratch for splitting the last, partial wave of tiles along K
+  // (nullptr: never split). Set by the caller; split and full_tiles are
+  // filled in by launch_gemm.
+  float *partial;
+  size_t partial_bytes;
+  int split;          // K slices per tile of the last wave (<= 1: no split)
+  int full_tiles;     // tiles computed whole before the split ones
 };
 
+// Launches the GEMM and, when the last wave of tiles is split along K, the
+// kernel that adds the slices and applies the epilogue.
 hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s);
+
+// Scratch bytes that let launch_gemm split the last wave of an M x N x K GEMM
+// on a 256-CU device (0: it would not split).
+size_t gemm_split_scratch_bytes(int64_t M, int64_t N, int64_t K);
 
 // o[T, A] = attention over qk [T, 2A] and vt [H, 128, Tp]
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
