@@ -208,7 +208,16 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cfg) -> str:
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = per_dispatch(d, counter)
         copy = [r for r in rows if "copy" in r[1].lower() or "elementwise" in r[1].lower()]
-        lib = [r for r in rows if "h3dit" in r[1]]
+        # library dispatches in order; a GEMM's slice-sum kernel counts with that GEMM
+        lib = []
+        for r in rows:
+            if "h3dit" not in r[1]:
+                continue
+            if "gemm_fixup" in r[1]:
+                assert lib, "slice-sum kernel before any GEMM"
+                lib[-1] = (lib[-1][0], lib[-1][1], lib[-1][2] + r[2])
+            else:
+                lib.append(r)
         assert copy and len(lib) >= len(KERNEL_ORDER), (counter, len(copy), len(lib))
         copy_kib = max(r[2] for r in copy)
         scales[counter] = COPY_BYTES / (copy_kib * 1024.0)

@@ -363,7 +363,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
 }
 
 // Sum of the K slices of split tile full_tiles + blockIdx.x (in slice order),
-// then the epilogue, with the thread -> output mapping of gemm_kernel.
+// then the epilogue, with the thread -> output mapping of gemm_kernel;
+// workgroup blockIdx.y takes feature blocks 2 y and 2 y + 1 of every wave.
 template <int EPI>
 __global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -378,7 +379,8 @@ __global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * (int)blockIdx.y + ii;
       const int64_t o = (i * 4 + j) * 512;
       f32x4 v = src[o];
       for (int sl = 1; sl < a.split; ++sl) v += src[(int64_t)sl * (32 * 512) + o];
@@ -439,7 +441,7 @@ static hipError_t launch_epi(const GemmArgs &a0, hipStream_t s) {
   hipLaunchKernelGGL(gemm_kernel<EPI>, dim3(grid), dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split <= 1) return e;
-  hipLaunchKernelGGL(gemm_fixup_kernel<EPI>, dim3(rem), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(gemm_fixup_kernel<EPI>, dim3(rem, 4), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
