@@ -91,6 +91,36 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z / (1.0f + expf(-2.0f * y));
 }
 
+// q or k: rotate the two adjacent pairs of the fp32 products, then round once;
+// q also takes the softmax factor log2(e)/sqrt(128) before its rounding, so that
+// attention scores leave the matrix cores in base-2 units.
+__device__ __forceinline__ bf16x4 qk_rope4(const GemmArgs &a, int t, int n, float v0, float v1,
+                                           float v2, float v3) {
+  const float u0 = v0, w0 = v1, u1 = v2, w1 = v3;
+  const int p = (n & 127) >> 1;  // pair index within the head (0..63)
+  const f32x4 cs = *reinterpret_cast<const f32x4 *>(a.table + ((int64_t)t * 64 + p) * 2);
+  const float sc = n < a.A ? kLog2eOverSqrt128 : 1.0f;
+  bf16x4 r;
+  r[0] = to_bf16((u0 * cs[0] - w0 * cs[1]) * sc);
+  r[1] = to_bf16((u0 * cs[1] + w0 * cs[0]) * sc);
+  r[2] = to_bf16((u1 * cs[2] - w1 * cs[3]) * sc);
+  r[3] = to_bf16((u1 * cs[3] + w1 * cs[2]) * sc);
+  return r;
+}
+
+__device__ __forceinline__ bf16x4 gelu4(float v0, float v1, float v2, float v3) {
+  bf16x4 r;
+  r[0] = to_bf16(gelu_tanh(v0));
+  r[1] = to_bf16(gelu_tanh(v1));
+  r[2] = to_bf16(gelu_tanh(v2));
+  r[3] = to_bf16(gelu_tanh(v3));
+  return r;
+}
+
+// token t of a V tile is stored at column t with bits 2 and 3 exchanged (the key
+// order of the attention kernel's P V fragments)
+__device__ __forceinline__ int vt_col(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+
 // Four consecutive outputs (features n .. n+3 of token t) through the epilogue.
 template <int EPI>
 __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0, float v1,
@@ -100,24 +130,12 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
     const int A2 = 2 * a.A;
     if (n < A2) {
       if (t >= a.M) return;
-      // q or k: rotate the two adjacent pairs of the fp32 products, then round
-      // once; q also takes the softmax factor log2(e)/sqrt(128) before its
-      // rounding, so that attention scores leave the matrix cores in base-2 units
-      const float u0 = v0, w0 = v1, u1 = v2, w1 = v3;
-      const int p = (n & 127) >> 1;  // pair index within the head (0..63)
-      const f32x4 cs = *reinterpret_cast<const f32x4 *>(a.table + ((int64_t)t * 64 + p) * 2);
-      const float sc = n < a.A ? kLog2eOverSqrt128 : 1.0f;
-      bf16x4 r;
-      r[0] = to_bf16((u0 * cs[0] - w0 * cs[1]) * sc);
-      r[1] = to_bf16((u0 * cs[1] + w0 * cs[0]) * sc);
-      r[2] = to_bf16((u1 * cs[2] - w1 * cs[3]) * sc);
-      r[3] = to_bf16((u1 * cs[3] + w1 * cs[2]) * sc);
-      *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * A2 + n) = r;
+      *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * A2 + n) =
+          qk_rope4(a, t, n, v0, v1, v2, v3);
     } else {
       if (t >= a.Mp) return;
       const int hv = n - A2;  // head * 128 + dim
-      // token t is stored at column t with bits 2 and 3 exchanged (see attention)
-      const int col = (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+      const int col = vt_col(t);
       bf16 *vt = static_cast<bf16 *>(a.out2) + (int64_t)hv * a.Mp + col;
       const bool live = t < a.M;
       vt[0] = to_bf16(live ? v0 : 0.0f);
@@ -147,12 +165,67 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
         f32x4{v0, v1, v2, v3};
   } else {  // EPI_GELU
     if (t >= a.M) return;
-    bf16x4 r;
-    r[0] = to_bf16(gelu_tanh(v0));
-    r[1] = to_bf16(gelu_tanh(v1));
-    r[2] = to_bf16(gelu_tanh(v2));
-    r[3] = to_bf16(gelu_tanh(v3));
-    *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * a.N + n) = r;
+    *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * a.N + n) =
+        gelu4(v0, v1, v2, v3);
+  }
+}
+
+// bf16 staging of a 256 x 256 output tile in LDS (element offset): 16-byte chunk
+// c of row r sits at chunk c ^ (2 (r & 15)), so the 16 rows written by a fragment
+// block and the whole rows read back both spread over all banks.
+__device__ __forceinline__ int stage_off(int row, int col) {
+  return row * 256 + ((((col >> 3) ^ ((row & 15) << 1))) << 3) + (col & 7);
+}
+
+// bf16 epilogue through LDS: the wave's results go to the staged tile (tokens x
+// features for q/k; features x tokens, columns in the attention's key order, for
+// V), then every thread stores whole 16-byte chunks of rows, so each store
+// instruction writes two contiguous 512-byte rows (instead of 2-byte scattered
+// stores for V). Used for the QKV epilogue (about 1.5 % faster there); the
+// GELU epilogue's direct 8-byte stores are as fast.
+template <int EPI>
+__device__ __forceinline__ void staged_bf16_epilogue(const GemmArgs &a, bf16 *lds, const f32x4 (&acc)[8][4],
+                                                     int n0, int t0, int wn, int wt, int r16, int kq) {
+  const int tid = threadIdx.x;
+  bool vtile = false;
+  if constexpr (EPI == EPI_QKV_ROPE) vtile = n0 >= 2 * a.A;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tl = wt * 64 + 16 * j + r16, fl = wn * 128 + 16 * i + 4 * kq;
+      const int t = t0 + tl, n = n0 + fl;
+      const f32x4 v = acc[i][j];
+      if constexpr (EPI == EPI_QKV_ROPE) {
+        if (vtile) {
+          const bool live = t < a.M;
+          const int col = vt_col(tl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lds[stage_off(fl + e, col)] = to_bf16(live ? v[e] : 0.0f);
+          continue;
+        }
+        const bf16x4 r = t < a.M ? qk_rope4(a, t, n, v[0], v[1], v[2], v[3]) : bf16x4{};
+        *reinterpret_cast<bf16x4 *>(lds + stage_off(tl, fl)) = r;
+      } else {
+        *reinterpret_cast<bf16x4 *>(lds + stage_off(tl, fl)) = gelu4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  __syncthreads();
+#pragma unroll 4
+  for (int q = tid; q < 256 * 32; q += 512) {
+    const int row = q >> 5, c = q & 31;
+    const bf16x8 val = *reinterpret_cast<const bf16x8 *>(lds + stage_off(row, 8 * c));
+    if (vtile) {  // row = feature of the V tile, 8 tokens per chunk
+      const int hv = n0 - 2 * a.A + row, t = t0 + 8 * c;
+      if (hv < a.A && t < a.Mp)
+        *reinterpret_cast<bf16x8 *>(static_cast<bf16 *>(a.out2) + (int64_t)hv * a.Mp + t) = val;
+    } else {  // row = token, 8 features per chunk
+      const int t = t0 + row, n = n0 + 8 * c;
+      const int ld = EPI == EPI_QKV_ROPE ? 2 * a.A : a.N;
+      const int nend = EPI == EPI_QKV_ROPE ? 2 * a.A : a.N;
+      if (t < a.M && n < nend)
+        *reinterpret_cast<bf16x8 *>(static_cast<bf16 *>(a.out) + (int64_t)t * ld + n) = val;
+    }
   }
 }
 
@@ -351,6 +424,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) dst[(i * 4 + j) * 512] = acc[i][j];
+    return;
+  }
+  if constexpr (EPI == EPI_QKV_ROPE) {
+    // every copy has landed and every wave has read its last fragments
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    staged_bf16_epilogue<EPI>(a, lds, acc, n0, t0, wn, wt, r16, kq);
     return;
   }
   const int nb = n0 + wn * 128 + 4 * kq, tb = t0 + wt * 64 + r16;
