@@ -281,6 +281,68 @@ def measure_stack(scfg, images: int, warmup: int):
     return sec, ok
 
 
+def measure_ulysses(cfg, G: int, steps: int, warmup: int):
+    """One GPU's share of a block under G-way Ulysses sequence parallelism: the
+    per-token kernels on T/G tokens (a block of T/G tokens with the same widths),
+    attention on H/G heads over all T tokens. The two all-to-alls (q, k, v from
+    tokens to heads before attention, o back after it) are not run: one GPU is
+    available, so the bytes each GPU would send are reported instead."""
+    import dataclasses
+    import torch
+    from joint_attention_dit_amd import binding as B
+
+    T, H, A = cfg.n_tokens, cfg.heads, cfg.attn_width
+    assert T % G == 0 and H % G == 0, (T, H, G)
+    Ts, Hs = T // G, H // G
+    text = cfg.text_tokens // G
+    cols = 64
+    assert (Ts - text) % cols == 0, (Ts, text)
+    rows = (Ts - text) // cols
+    share = dataclasses.replace(cfg, name=f"{cfg.name}_share{G}", text_tokens=text,
+                                images=((rows, cols, 0),),
+                                description=f"{cfg.name} share of {G}: {text} text + {rows}x{cols} image tokens")
+    ms, stage_ms, ok = measure(share, steps, warmup)
+
+    # attention of the share: Hs heads over all T tokens
+    acfg = B.make_config(cfg.hidden, Hs, cfg.ffn, T)
+    Tp = B.h3dit_padded_tokens(T)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    qk = torch.randn(T, 2 * Hs * 128, device="cuda", generator=g)
+    qk[:, :Hs * 128] *= 12.0 / 128 ** 0.5  # base-2 score spread like the block's (std ~ 12)
+    qk = qk.to(torch.bfloat16)
+    vt = torch.randn(Hs, 128, Tp, device="cuda", generator=g).to(torch.bfloat16)
+    o = torch.empty(T, Hs * 128, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        B.h3dit_attention(acfg, qk, vt, o, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        B.h3dit_attention(acfg, qk, vt, o, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    att_ms = e0.elapsed_time(e1) / steps
+    ok = ok and bool(torch.isfinite(o).all().item())
+
+    kernels = dict(stage_ms)
+    kernels["attention"] = att_ms
+    total = sum(kernels.values())
+    flops = 2.0 * Ts * (3 * A * cfg.hidden + A * cfg.hidden + 2 * cfg.hidden * cfg.ffn) \
+        + 4.0 * T * T * Hs * 128 + 2.0 * 6 * cfg.hidden * cfg.hidden
+    qkv_bytes = Ts * 3 * A * 2            # this GPU's q, k, v before the first all-to-all
+    o_bytes = T * Hs * 128 * 2            # this GPU's attention output before the second
+    return {
+        "gpus": G, "tokens_per_gpu": Ts, "heads_per_gpu": Hs, "share_workload": share.description,
+        "ms_per_block_compute": round(total, 4),
+        "tflops_per_gpu": round(flops / (total * 1e-3) / 1e12, 1),
+        "pct_bf16_mfma_peak": round(100 * flops / (total * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "kernels_ms": {k: round(v, 4) for k, v in kernels.items()},
+        "alltoall_bytes_sent_per_gpu": {"qkv": qkv_bytes * (G - 1) // G, "o": o_bytes * (G - 1) // G},
+        "output_finite": ok,
+    }
+
+
 def stack_flops(scfg) -> float:
     b = scfg.block
     per_eval = scfg.n_blocks * block_flops(b) + 2.0 * 2 * b.image_tokens * b.hidden * scfg.patch_features \
@@ -338,6 +400,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
     ap.add_argument("--stack", action="store_true",
                     help="time the full DiT stack (50 blocks, 6 steps at 2048x2048) instead")
+    ap.add_argument("--ulysses", type=int, default=0, metavar="G",
+                    help="time one GPU's share of G-way Ulysses sequence parallelism instead")
     ap.add_argument("--traffic-run", action="store_true",
                     help="one 1 GiB copy + one block (the command the HBM counter passes profile)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -361,6 +425,16 @@ def main():
     cfg = CONFIGS[args.workload]
     if args.traffic_run:
         traffic_run(cfg)
+        return
+    if args.ulysses:
+        G = args.ulysses
+        u = measure_ulysses(cfg, G, max(args.steps // 2, 1), max(args.warmup // 2, 1))
+        print(json.dumps({
+            "metric": f"one GPU's share of a {G}-way Ulysses-parallel block (compute only)",
+            "value": round(cfg.n_tokens / (u["ms_per_block_compute"] * 1e-3), 1),
+            "unit": "block-tokens/s of the whole job if the all-to-alls are hidden",
+            "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": cfg.description}, "ulysses": u}), flush=True)
         return
     if args.stack:
         from joint_attention_dit_amd.inputs import STACK_CONFIGS
