@@ -241,10 +241,12 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cfg) -> str:
     return "\n".join(lines) + "\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n"
 
 
-def measure_stack(scfg, images: int, warmup: int):
+def measure_stack(scfg, images: int, warmup: int, mod_table: bool = True):
     """Seconds per image of DiT compute: `scfg.steps` evaluations of the whole
     stack (patch embedding, n_blocks blocks, final layer) with an Euler update
-    after each, on seeded random-init weights resident in HBM."""
+    after each, on seeded random-init weights resident in HBM. With mod_table,
+    every block's and the final layer's modulation for all steps is computed
+    first in one pass over each AdaLN weight (inside the timed region)."""
     import torch
     from joint_attention_dit_amd import binding as B
     from joint_attention_dit_amd.inputs import make_stack_inputs
@@ -259,12 +261,24 @@ def measure_stack(scfg, images: int, warmup: int):
     v = torch.empty_like(latent)
     stream = torch.cuda.current_stream()
 
+    conds = torch.stack(list(inp["conds"])).contiguous()
+    table = torch.empty(scfg.steps, scfg.n_blocks + 1, 6 * scfg.block.hidden, dtype=torch.float64,
+                        device="cuda")
+
     def image():
         latent.copy_(latent0)
-        for cond in inp["conds"]:
-            B.h3dit_dit_forward(cfg, st, inp["w_patch"], inp["w_ada_final"], inp["w_final"],
-                                inp["blocks"], latent, inp["text"], cond, inp["positions"], v, ws,
-                                stream)
+        if mod_table:
+            B.h3dit_dit_modulation_table(cfg, st, inp["w_ada_final"], inp["blocks"], conds, table,
+                                         stream)
+        for k, cond in enumerate(inp["conds"]):
+            if mod_table:
+                B.h3dit_dit_forward_mod(cfg, st, inp["w_patch"], inp["w_final"], inp["blocks"],
+                                        latent, inp["text"], table[k], inp["positions"], v, ws,
+                                        stream)
+            else:
+                B.h3dit_dit_forward(cfg, st, inp["w_patch"], inp["w_ada_final"], inp["w_final"],
+                                    inp["blocks"], latent, inp["text"], cond, inp["positions"], v,
+                                    ws, stream)
             B.h3dit_latent_step(latent, v, 1.0 / scfg.steps, stream)
 
     for _ in range(warmup):
@@ -400,6 +414,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
     ap.add_argument("--stack", action="store_true",
                     help="time the full DiT stack (50 blocks, 6 steps at 2048x2048) instead")
+    ap.add_argument("--no-mod-table", action="store_true",
+                    help="with --stack: compute each block's modulation per step instead of a table")
     ap.add_argument("--ulysses", type=int, default=0, metavar="G",
                     help="time one GPU's share of G-way Ulysses sequence parallelism instead")
     ap.add_argument("--traffic-run", action="store_true",
@@ -439,10 +455,12 @@ def main():
     if args.stack:
         from joint_attention_dit_amd.inputs import STACK_CONFIGS
         scfg = STACK_CONFIGS["dit_2048"]
-        sec, ok = measure_stack(scfg, images=max(args.steps // 10, 1), warmup=1 if args.warmup else 0)
+        sec, ok = measure_stack(scfg, images=max(args.steps // 10, 1), warmup=1 if args.warmup else 0,
+                                mod_table=not args.no_mod_table)
         fl = stack_flops(scfg)
         print(json.dumps({
             "metric": "DiT compute images/s (50 blocks x 6 denoising steps, 2048x2048)",
+            "modulation": "per-step table" if not args.no_mod_table else "per block call",
             "value": round(1.0 / sec, 4), "unit": "images/s", "n_gpus": 1,
             "ms_per_image": round(sec * 1e3, 2),
             "ms_per_block": round(sec * 1e3 / (scfg.n_blocks * scfg.steps), 4),

@@ -123,6 +123,14 @@ int h3dit_block_forward_timed(const h3dit_config *cfg, const void *x, const floa
 int h3dit_modulation(const h3dit_config *cfg, const void *w_ada, const float *cond,
                      double *mod, void *stream);
 
+/* Step 1 for n conditioning vectors at once (AdaLN caching; vLLM blog, "Faster
+ * DiT": the conditioning projections are precomputed once per request):
+ *   conds [n, D] fp32, mods [n, 6D] fp64 (caller-owned, 16-byte aligned);
+ *   mods[s] is bitwise what h3dit_modulation returns for conds[s], while each
+ *   weight is read once per 8 vectors. 1 <= n <= 4096. */
+int h3dit_modulation_table(const h3dit_config *cfg, const void *w_ada, const float *conds,
+                           int n, double *mods, void *stream);
+
 /* Steps 2 and 7, RMSNorm + modulation (spec page, "RMS Normalization"):
  * h[T, D] bf16 = bf16( x / sqrt(mean(x^2) + eps) * (1 + scale) + shift ),
  * computed in fp64; x is [T, D] of dtype x_dtype; shift, scale are fp64 [D]. */
@@ -224,6 +232,27 @@ int h3dit_dit_forward(const h3dit_config *cfg, const h3dit_stack_config *st,
                       const h3dit_stack_weights *w, const float *latent, const float *text,
                       const float *cond, const int32_t *positions, float *v, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* Every block's modulation and the final layer's for n_steps denoising steps,
+ * one pass over each AdaLN weight (AdaLN caching, as for h3dit_modulation_table):
+ *   conds [n_steps, D] fp32 (one conditioning vector per step);
+ *   table [n_steps][n_blocks + 1][6D] fp64, caller-owned: entry [s][b] for
+ *   b < n_blocks is block b's modulation for conds[s], entry [s][n_blocks] holds
+ *   the final layer's (shift, scale) in its first 2D values (the rest is left
+ *   untouched). w->w_patch, w->w_final and the blocks' other weights are not read.
+ * 1 <= n_steps <= 4096. */
+int h3dit_dit_modulation_table(const h3dit_config *cfg, const h3dit_stack_config *st,
+                               const h3dit_stack_weights *w, const float *conds, int n_steps,
+                               double *table, void *stream);
+
+/* h3dit_dit_forward with the modulation taken from one step's row of the table
+ * above (mods = table + s * (n_blocks + 1) * 6D) instead of computed from cond;
+ * the blocks' w_ada and w->w_ada_final are not read. The result is bitwise that
+ * of h3dit_dit_forward with conds[s]. */
+int h3dit_dit_forward_mod(const h3dit_config *cfg, const h3dit_stack_config *st,
+                          const h3dit_stack_weights *w, const float *latent, const float *text,
+                          const double *mods, const int32_t *positions, float *v, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /* latent[i] += dt * v[i] for i < n (fp32): the explicit Euler update between
  * denoising steps. */

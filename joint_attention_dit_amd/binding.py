@@ -27,7 +27,8 @@ EXPORTED = (
     "h3dit_attention", "h3dit_out_proj_residual", "h3dit_mlp_up_gelu",
     "h3dit_mlp_down_residual", "h3dit_linear_f32", "h3dit_stack_workspace_size",
     "h3dit_dit_forward", "h3dit_latent_step", "h3dit_padded_tokens", "h3dit_status_string",
-    "h3dit_last_error",
+    "h3dit_last_error", "h3dit_modulation_table", "h3dit_dit_modulation_table",
+    "h3dit_dit_forward_mod",
 )
 
 
@@ -92,6 +93,11 @@ def load_library() -> ctypes.CDLL:
         "h3dit_dit_forward": [cfgp, ctypes.POINTER(StackConfig), ctypes.POINTER(StackWeights),
                               vp, vp, vp, vp, vp, vp, sz, vp],
         "h3dit_latent_step": [vp, vp, ctypes.c_float, ctypes.c_int64, vp],
+        "h3dit_modulation_table": [cfgp, vp, vp, ctypes.c_int, vp, vp],
+        "h3dit_dit_modulation_table": [cfgp, ctypes.POINTER(StackConfig),
+                                       ctypes.POINTER(StackWeights), vp, ctypes.c_int, vp, vp],
+        "h3dit_dit_forward_mod": [cfgp, ctypes.POINTER(StackConfig), ctypes.POINTER(StackWeights),
+                                  vp, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -191,6 +197,13 @@ def h3dit_modulation(cfg: Config, w_ada, cond, mod, stream=None) -> None:
                                            _stream(stream)), "h3dit_modulation")
 
 
+def h3dit_modulation_table(cfg: Config, w_ada, conds, mods, stream=None) -> None:
+    """conds [n, D] fp32 -> mods [n, 6D] fp64 (one pass over w_ada)."""
+    _check(load_library().h3dit_modulation_table(ctypes.byref(cfg), _ptr(w_ada), _ptr(conds),
+                                                 int(conds.shape[0]), _ptr(mods), _stream(stream)),
+           "h3dit_modulation_table")
+
+
 def h3dit_rmsnorm_modulate(cfg: Config, x, shift, scale, h, stream=None) -> None:
     _check(load_library().h3dit_rmsnorm_modulate(ctypes.byref(cfg), _ptr(x), _dtype_code(x),
                                                  _ptr(shift), _ptr(scale), _ptr(h),
@@ -255,6 +268,34 @@ def h3dit_dit_forward(cfg: Config, st: StackConfig, w_patch, w_ada_final, w_fina
         ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), _ptr(latent), _ptr(text),
         _ptr(cond), _ptr(positions), _ptr(v), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)), "h3dit_dit_forward")
+
+
+def _stack_weights(w_patch, w_ada_final, w_final, blocks):
+    arr = (Weights * max(len(blocks), 1))(*[weights_struct(b) for b in blocks])
+    sw = StackWeights(_ptr(w_patch), _ptr(w_ada_final), _ptr(w_final),
+                      ctypes.cast(arr, ctypes.POINTER(Weights)))
+    return sw, arr  # the array must outlive the call
+
+
+def h3dit_dit_modulation_table(cfg: Config, st: StackConfig, w_ada_final,
+                               blocks: Sequence[Dict[str, torch.Tensor]], conds, table,
+                               stream=None) -> None:
+    """conds [S, D] fp32 -> table [S, n_blocks + 1, 6D] fp64."""
+    sw, arr = _stack_weights(None, w_ada_final, None, blocks)
+    _check(load_library().h3dit_dit_modulation_table(
+        ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), _ptr(conds), int(conds.shape[0]),
+        _ptr(table), _stream(stream)), "h3dit_dit_modulation_table")
+
+
+def h3dit_dit_forward_mod(cfg: Config, st: StackConfig, w_patch, w_final,
+                          blocks: Sequence[Dict[str, torch.Tensor]], latent, text, mods, positions,
+                          v, workspace, stream=None) -> None:
+    """h3dit_dit_forward with the modulation from one step's table row mods."""
+    sw, arr = _stack_weights(w_patch, None, w_final, blocks)
+    _check(load_library().h3dit_dit_forward_mod(
+        ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), _ptr(latent), _ptr(text),
+        _ptr(mods), _ptr(positions), _ptr(v), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "h3dit_dit_forward_mod")
 
 
 def h3dit_latent_step(latent: torch.Tensor, v: torch.Tensor, dt: float, stream=None) -> None:

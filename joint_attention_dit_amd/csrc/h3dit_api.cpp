@@ -143,17 +143,21 @@ GemmArgs gemm_args(const void *x, const void *w, int64_t M, int64_t N, int64_t K
   return g;
 }
 
+// mod_in: the block's modulation (fp64 [6D]) computed beforehand, or NULL to
+// compute it from cond and w->w_ada.
 int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, const h3dit_weights *w,
                  const int32_t *positions, float *out, void *ws, size_t ws_bytes, void *stream,
-                 void *const *events, int n_events) {
+                 void *const *events, int n_events, const double *mod_in = nullptr) {
   CHECK_CFG(cfg);
   if (!w) return fail(H3DIT_EINVAL, "w is NULL");
   CHECK_PTR(x);
-  CHECK_PTR(cond);
   CHECK_PTR(positions);
   CHECK_PTR(out);
   CHECK_PTR(ws);
-  CHECK_PTR(w->w_ada);
+  if (!mod_in) {
+    CHECK_PTR(cond);
+    CHECK_PTR(w->w_ada);
+  }
   CHECK_PTR(w->w_qkv);
   CHECK_PTR(w->w_o);
   CHECK_PTR(w->w_up);
@@ -176,7 +180,7 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  double *mod = at<double>(ws, p.mod);
+  const double *mod = mod_in ? mod_in : at<double>(ws, p.mod);
   float *table = at<float>(ws, p.table);
   void *h = at<void>(ws, p.h);
   void *qk = at<void>(ws, p.qk);
@@ -193,7 +197,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   };
 
   LAUNCH(mark(0), "event record");
-  LAUNCH(launch_modulation(w->w_ada, cond, mod, 6 * D, D, s), "modulation");
+  if (!mod_in)
+    LAUNCH(launch_modulation(w->w_ada, cond, at<double>(ws, p.mod), 6 * D, D, s), "modulation");
   LAUNCH(mark(1), "event record");
   LAUNCH(launch_rope_table(positions, table, T, cfg->rope_base, s), "rope table");
   LAUNCH(mark(2), "event record");
@@ -303,21 +308,24 @@ StackPlan make_stack_plan(const h3dit_config *cfg, const h3dit_stack_config *st)
   return p;
 }
 
+// mods: every block's modulation and the final layer's, fp64 [(n_blocks + 1) * 6D]
+// (entry n_blocks holds the final layer's shift and scale in its first 2D values),
+// or NULL to compute them from cond.
 int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_stack_weights *w,
              const float *latent, const float *text, const float *cond, const int32_t *positions,
-             float *v, void *ws, size_t ws_bytes, void *stream) {
+             float *v, void *ws, size_t ws_bytes, void *stream, const double *mods = nullptr) {
   {
     const int st_ = check_stack(cfg, st);
     if (st_ != H3DIT_OK) return st_;
   }
   if (!w) return fail(H3DIT_EINVAL, "w is NULL");
   CHECK_PTR(w->w_patch);
-  CHECK_PTR(w->w_ada_final);
+  if (!mods) CHECK_PTR(w->w_ada_final);
   CHECK_PTR(w->w_final);
   if (st->n_blocks > 0 && !w->blocks) return fail(H3DIT_EINVAL, "w->blocks is NULL");
   CHECK_PTR(latent);
   if (st->text_tokens > 0) CHECK_PTR(text);
-  CHECK_PTR(cond);
+  if (!mods) CHECK_PTR(cond);
   CHECK_PTR(positions);
   CHECK_PTR(v);
   CHECK_PTR(ws);
@@ -331,10 +339,10 @@ int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_
   }
   for (int l = 0; l < st->n_blocks; ++l) {  // every block's weights, before anything is enqueued
     const h3dit_weights &b = w->blocks[l];
-    if (!b.w_ada || !b.w_qkv || !b.w_o || !b.w_up || !b.w_down)
+    if ((!mods && !b.w_ada) || !b.w_qkv || !b.w_o || !b.w_up || !b.w_down)
       return fail(H3DIT_EINVAL, "block %d has a NULL weight pointer", l);
-    if (!aligned16(b.w_ada) || !aligned16(b.w_qkv) || !aligned16(b.w_o) || !aligned16(b.w_up) ||
-        !aligned16(b.w_down))
+    if ((!mods && !aligned16(b.w_ada)) || !aligned16(b.w_qkv) || !aligned16(b.w_o) ||
+        !aligned16(b.w_up) || !aligned16(b.w_down))
       return fail(H3DIT_EALIGN, "block %d has a weight pointer that is not 16-byte aligned", l);
   }
 
@@ -357,15 +365,20 @@ int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_
   float *cur = xa, *nxt = xb;
   for (int l = 0; l < st->n_blocks; ++l) {
     const int rc = forward_impl(&bc, cur, cond, &w->blocks[l], positions, nxt, at<void>(ws, p.block),
-                                p.block_bytes, stream, nullptr, 0);
+                                p.block_bytes, stream, nullptr, 0,
+                                mods ? mods + (size_t)l * 6 * D : nullptr);
     if (rc != H3DIT_OK) return rc;
     float *t = cur;
     cur = nxt;
     nxt = t;
   }
   // final layer on the image tokens
-  LAUNCH(launch_modulation(w->w_ada_final, cond, modf, 2 * D, D, s), "final modulation");
-  LAUNCH(launch_rmsnorm_modulate_f32out(cur + (size_t)text_tokens * D, true, modf, modf + D, hf, Ti,
+  const double *mf = modf;
+  if (mods)
+    mf = mods + (size_t)st->n_blocks * 6 * D;
+  else
+    LAUNCH(launch_modulation(w->w_ada_final, cond, modf, 2 * D, D, s), "final modulation");
+  LAUNCH(launch_rmsnorm_modulate_f32out(cur + (size_t)text_tokens * D, true, mf, mf + D, hf, Ti,
                                         D, cfg->eps, s),
          "final rmsnorm");
   LAUNCH(launch_gemm_f32(hf, w->w_final, vt, Ti, F, D, F, s), "final projection");
@@ -391,6 +404,45 @@ int h3dit_dit_forward(const h3dit_config *cfg, const h3dit_stack_config *st,
                       const float *cond, const int32_t *positions, float *v, void *workspace,
                       size_t workspace_bytes, void *stream) {
   return dit_impl(cfg, st, w, latent, text, cond, positions, v, workspace, workspace_bytes, stream);
+}
+
+int h3dit_dit_modulation_table(const h3dit_config *cfg, const h3dit_stack_config *st,
+                               const h3dit_stack_weights *w, const float *conds, int n_steps,
+                               double *table, void *stream) {
+  const int rc = check_stack(cfg, st);
+  if (rc != H3DIT_OK) return rc;
+  if (!w) return fail(H3DIT_EINVAL, "w is NULL");
+  CHECK_PTR(w->w_ada_final);
+  if (st->n_blocks > 0 && !w->blocks) return fail(H3DIT_EINVAL, "w->blocks is NULL");
+  CHECK_PTR(conds);
+  CHECK_PTR(table);
+  if (n_steps < 1 || n_steps > 4096)
+    return fail(H3DIT_EINVAL, "n_steps must be in [1, 4096] (got %d)", n_steps);
+  for (int l = 0; l < st->n_blocks; ++l) {
+    const void *wa = w->blocks[l].w_ada;
+    if (!wa) return fail(H3DIT_EINVAL, "block %d has a NULL w_ada", l);
+    if (!aligned16(wa)) return fail(H3DIT_EALIGN, "block %d w_ada is not 16-byte aligned", l);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int D = cfg->hidden;
+  const int64_t stride = (int64_t)(st->n_blocks + 1) * 6 * D;
+  for (int l = 0; l < st->n_blocks; ++l)
+    LAUNCH(launch_modulation_multi(w->blocks[l].w_ada, conds, n_steps, table + (int64_t)l * 6 * D,
+                                   stride, 6 * D, D, s),
+           "block modulation table");
+  LAUNCH(launch_modulation_multi(w->w_ada_final, conds, n_steps,
+                                 table + (int64_t)st->n_blocks * 6 * D, stride, 2 * D, D, s),
+         "final modulation table");
+  return ok();
+}
+
+int h3dit_dit_forward_mod(const h3dit_config *cfg, const h3dit_stack_config *st,
+                          const h3dit_stack_weights *w, const float *latent, const float *text,
+                          const double *mods, const int32_t *positions, float *v, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  CHECK_PTR(mods);
+  return dit_impl(cfg, st, w, latent, text, nullptr, positions, v, workspace, workspace_bytes,
+                  stream, mods);
 }
 
 int h3dit_latent_step(float *latent, const float *v, float dt, int64_t n, void *stream) {
@@ -437,6 +489,20 @@ int h3dit_modulation(const h3dit_config *cfg, const void *w_ada, const float *co
   LAUNCH(launch_modulation(w_ada, cond, mod, 6 * cfg->hidden, cfg->hidden,
                            static_cast<hipStream_t>(stream)),
          "modulation");
+  return ok();
+}
+
+int h3dit_modulation_table(const h3dit_config *cfg, const void *w_ada, const float *conds,
+                           int n, double *mods, void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(w_ada);
+  CHECK_PTR(conds);
+  CHECK_PTR(mods);
+  if (n < 1 || n > 4096) return fail(H3DIT_EINVAL, "n must be in [1, 4096] (got %d)", n);
+  const int D = cfg->hidden;
+  LAUNCH(launch_modulation_multi(w_ada, conds, n, mods, 6 * (int64_t)D, 6 * D, D,
+                                 static_cast<hipStream_t>(stream)),
+         "modulation table");
   return ok();
 }
 

@@ -11,6 +11,11 @@ namespace h3dit {
 hipError_t launch_modulation(const void *w, const float *cond, double *mod, int rows, int cols,
                              hipStream_t s);
 
+// mods[k * mod_stride + r] = (W . conds[k])[r] for k < n, each bitwise equal to
+// launch_modulation with conds[k] (W read once per 8 vectors)
+hipError_t launch_modulation_multi(const void *w, const float *conds, int n, double *mods,
+                                   int64_t mod_stride, int rows, int cols, hipStream_t s);
+
 // h[T, D] (bf16) = bf16(rmsnorm(x) * (1 + scale) + shift), fp64 math; D % 8 == 0
 hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *shift,
                                    const double *scale, void *h, int T, int D, float eps,

@@ -33,6 +33,60 @@ __global__ __launch_bounds__(256) void modulation_kernel(const bf16 *__restrict_
   if (lane == 0) mod[row] = acc;
 }
 
+// The same products for up to MAXS conditioning vectors per pass over the
+// weights (AdaLN caching: the vLLM blog, "Faster DiT", precomputes the
+// conditioning projections): lane l accumulates, for each vector, exactly the
+// sequence of products the one-vector kernel accumulates, and the same
+// shuffle tree sums the lanes, so mods[s] is bitwise the one-vector result.
+constexpr int MAXS = 8;
+__global__ __launch_bounds__(256) void modulation_multi_kernel(const bf16 *__restrict__ w,
+                                                               const float *__restrict__ conds,
+                                                               int n, double *__restrict__ mods,
+                                                               int64_t mod_stride, int rows, int cols) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const bf16 *wr = w + (int64_t)row * cols;
+  const int chunks = cols >> 3;
+  double acc[MAXS];
+#pragma unroll
+  for (int k = 0; k < MAXS; ++k) acc[k] = 0.0;
+  for (int c = lane; c < chunks; c += 64) {
+    const bf16x8 wv = *reinterpret_cast<const bf16x8 *>(wr + c * 8);
+#pragma unroll
+    for (int k = 0; k < MAXS; ++k) {
+      if (k < n) {
+        const float *cond = conds + (int64_t)k * cols;
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cond + c * 8);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cond + c * 8 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[k] += (double)(float)wv[j] * (double)c0[j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[k] += (double)(float)wv[4 + j] * (double)c1[j];
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < MAXS; ++k) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc[k] += __shfl_xor(acc[k], off, 64);
+    if (k < n && lane == 0) mods[k * mod_stride + row] = acc[k];
+  }
+}
+
+hipError_t launch_modulation_multi(const void *w, const float *conds, int n, double *mods,
+                                   int64_t mod_stride, int rows, int cols, hipStream_t s) {
+  const int blocks = (int)ceil_div(rows, 4);
+  for (int k0 = 0; k0 < n; k0 += MAXS) {
+    hipLaunchKernelGGL(modulation_multi_kernel, dim3(blocks), dim3(256), 0, s,
+                       static_cast<const bf16 *>(w), conds + (int64_t)k0 * cols, min(MAXS, n - k0),
+                       mods + k0 * mod_stride, mod_stride, rows, cols);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_modulation(const void *w, const float *cond, double *mod, int rows, int cols,
                              hipStream_t s) {
   const int blocks = (int)ceil_div(rows, 4);

@@ -200,3 +200,38 @@ def test_latent_step_validation(lib):
     assert lib.h3dit_latent_step(None, 0x100000000, 0.5, 10, None) == B.H3DIT_EINVAL
     assert lib.h3dit_latent_step(0x100000000, 0x200000000, 0.5, 0, None) == B.H3DIT_EINVAL
     assert lib.h3dit_latent_step(0x100000000, 0x200000000, float("nan"), 4, None) == B.H3DIT_EINVAL
+
+
+def test_modulation_table_validation(lib):
+    cfg = B.make_config(256, 2, 1024, 24)
+    a, c, m = 0x100000000, 0x200000000, 0x300000000
+    assert lib.h3dit_modulation_table(ctypes.byref(cfg), a, c, 0, m, None) == B.H3DIT_EINVAL
+    assert lib.h3dit_modulation_table(ctypes.byref(cfg), a, c, 4097, m, None) == B.H3DIT_EINVAL
+    assert lib.h3dit_modulation_table(ctypes.byref(cfg), None, c, 6, m, None) == B.H3DIT_EINVAL
+    assert lib.h3dit_modulation_table(ctypes.byref(cfg), a, c, 6, m + 8, None) == B.H3DIT_EALIGN
+
+
+def test_dit_modulation_table_and_forward_mod_validation(lib):
+    cfg = B.make_config(5376, 56, 14336, 4352, B.H3DIT_F32)
+    st = stack_cfg()
+    arr = (B.Weights * 2)(*[B.Weights(*[0x20000000000 + 0x1000000000 * (5 * b + j)
+                                        for j in range(5)]) for b in range(2)])
+    sw = B.StackWeights(0x100000000, 0x200000000, 0x300000000,
+                        ctypes.cast(arr, ctypes.POINTER(B.Weights)))
+    conds, table = 0x400000000, 0x500000000
+    tab = lib.h3dit_dit_modulation_table
+    assert tab(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), conds, 0, table, None) == B.H3DIT_EINVAL
+    assert tab(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), None, 6, table, None) == B.H3DIT_EINVAL
+    arr[1].w_ada = 0x20000000004  # misaligned block weight
+    assert tab(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), conds, 6, table, None) == B.H3DIT_EALIGN
+    arr[1].w_ada = None
+    assert tab(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), conds, 6, table, None) == B.H3DIT_EINVAL
+    assert "w_ada" in lib.h3dit_last_error().decode()
+    # with a table the AdaLN weights are not needed, but the table is
+    fwd = lib.h3dit_dit_forward_mod
+    args = (0x600000000, 0x700000000)  # latent, text
+    assert fwd(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), *args, None, 0x800000000,
+               0x900000000, 0xa00000000, 1 << 40, None) == B.H3DIT_EINVAL
+    assert "mods" in lib.h3dit_last_error().decode()
+    assert fwd(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), *args, 0xb00000000,
+               0x800000000, 0x900000000, 0xa00000000, 4096, None) == B.H3DIT_EWORKSPACE

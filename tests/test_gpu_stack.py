@@ -117,3 +117,52 @@ def test_stack_one_block_full_width():
     g_vs, _ = gpu_stack(scfg, inp)
     r_vs, _ = oracle_stack(scfg, inp)
     assert_block_parity(g_vs[0], r_vs[0], "full-width one-block DiT v")
+
+
+def test_modulation_table_bitwise_equals_one_vector_calls():
+    """Several conditioning vectors per pass over W_ada (9: two passes of 8 and 1)
+    give exactly the per-vector results."""
+    scfg = STACK_CONFIGS["tiny_stack"]
+    inp = make_stack_inputs(scfg, seed=3)
+    cfg = B.config_from(scfg.block)
+    D = scfg.block.hidden
+    w_ada = inp["blocks"][0]["w_ada"].cuda()
+    g = torch.Generator().manual_seed(11)
+    conds = (torch.randn(9, D, generator=g) * 3).cuda()
+    table = torch.empty(9, 6 * D, dtype=torch.float64, device="cuda")
+    B.h3dit_modulation_table(cfg, w_ada, conds, table)
+    for s in range(9):
+        one = torch.empty(6 * D, dtype=torch.float64, device="cuda")
+        B.h3dit_modulation(cfg, w_ada, conds[s].contiguous(), one)
+        assert torch.equal(table[s], one), s
+
+
+def test_stack_with_modulation_table_bitwise_equals_stack():
+    """All steps of the tiny stack: the modulation taken from the precomputed
+    table (every AdaLN weight read once) leaves every v and the final latent
+    bit-identical."""
+    scfg = STACK_CONFIGS["tiny_stack"]
+    say(f"[stack] modulation table, {scfg.description}")
+    inp = make_stack_inputs(scfg, seed=0)
+    g_vs, g_lat = gpu_stack(scfg, inp)
+    cfg = B.config_from(scfg.block)
+    gh, gw = scfg.grid
+    nb = len(inp["blocks"])
+    st = B.StackConfig(nb, scfg.channels, scfg.patch, gh, gw, scfg.block.text_tokens)
+    ws = torch.empty(B.h3dit_stack_workspace_size(cfg, st), dtype=torch.uint8, device="cuda")
+    dev = lambda t: t.to("cuda").contiguous()
+    dblocks = [{k: dev(v) for k, v in b.items()} for b in inp["blocks"]]
+    conds = torch.stack([c for c in inp["conds"]]).cuda().contiguous()
+    D = scfg.block.hidden
+    table = torch.full((len(inp["conds"]), nb + 1, 6 * D), float("nan"), dtype=torch.float64,
+                       device="cuda")
+    B.h3dit_dit_modulation_table(cfg, st, dev(inp["w_ada_final"]), dblocks, conds, table)
+    latent = dev(inp["latent"]).clone()
+    v = torch.empty_like(latent)
+    for k in range(len(inp["conds"])):
+        B.h3dit_dit_forward_mod(cfg, st, dev(inp["w_patch"]), dev(inp["w_final"]), dblocks, latent,
+                                dev(inp["text"]), table[k].contiguous(), dev(inp["positions"]), v,
+                                ws)
+        assert np.array_equal(v.cpu().double().numpy(), g_vs[k]), k
+        B.h3dit_latent_step(latent, v, DT)
+    assert np.array_equal(latent.cpu().double().numpy(), g_lat)
