@@ -183,8 +183,8 @@ def gelu_tanh(z: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 def block_forward(x: np.ndarray, cond: np.ndarray, w: Dict[str, np.ndarray], pos: np.ndarray,
                   heads: int, eps: float = 1e-6, rope_base: float = 10000.0,
-                  mode: str = "contract", rows: Optional[np.ndarray] = None
-                  ) -> Dict[str, np.ndarray]:
+                  mode: str = "contract", rows: Optional[np.ndarray] = None,
+                  linears: str = "bf16") -> Dict[str, np.ndarray]:
     """One DiT block. All array inputs float64 (bf16 / fp32 values widened exactly).
 
     x [T, D], cond [D], w: w_ada [6D, D], w_qkv [3A, D], w_o [D, A],
@@ -195,6 +195,16 @@ def block_forward(x: np.ndarray, cond: np.ndarray, w: Dict[str, np.ndarray], pos
     o, x1, h2, u, out) as float64.
     """
     assert mode in ("exact", "contract")
+    assert linears in ("bf16", "mxfp8")
+    # the four linears: plain products, or both operands quantised to MXFP8
+    # along K first (oracle/mxfp8.py; contract mode only, where the inputs are
+    # the bf16 operands of the GPU path)
+    if linears == "mxfp8":
+        assert mode == "contract"
+        from . import mxfp8
+        lin = mxfp8.linear
+    else:
+        lin = lambda a, b: a @ b.T
     T, D = x.shape
     A = w["w_qkv"].shape[0] // 3
     dh = A // heads
@@ -208,9 +218,9 @@ def block_forward(x: np.ndarray, cond: np.ndarray, w: Dict[str, np.ndarray], pos
 
     # a3: projections; k and v over all tokens, q over the requested rows
     w_q, w_k, w_v = w["w_qkv"][:A], w["w_qkv"][A:2 * A], w["w_qkv"][2 * A:]
-    q = (h1[r] @ w_q.T).reshape(len(r), heads, dh)
-    k = (h1 @ w_k.T).reshape(T, heads, dh)
-    v = _round(h1 @ w_v.T, mode).reshape(T, heads, dh)
+    q = lin(h1[r], w_q).reshape(len(r), heads, dh)
+    k = lin(h1, w_k).reshape(T, heads, dh)
+    v = _round(lin(h1, w_v), mode).reshape(T, heads, dh)
 
     # a4: RoPE on q and k; each is rounded to bf16 once, after the rotation
     # (and, for q, after the softmax scale)
@@ -222,12 +232,12 @@ def block_forward(x: np.ndarray, cond: np.ndarray, w: Dict[str, np.ndarray], pos
     o = attention(q, k, v, mode).reshape(len(r), A)
 
     # a6: output projection + gated residual
-    x1 = x[r] + mv["gate1"] * (o @ w["w_o"].T)
+    x1 = x[r] + mv["gate1"] * lin(o, w["w_o"])
 
     # a7 .. a9: modulated norm, GELU MLP, gated residual
     h2 = modulated_norm(x1, mv["shift2"], mv["scale2"], eps, mode)
-    u = _round(gelu_tanh(h2 @ w["w_up"].T), mode)
-    out = x1 + mv["gate2"] * (u @ w["w_down"].T)
+    u = _round(gelu_tanh(lin(h2, w["w_up"])), mode)
+    out = x1 + mv["gate2"] * lin(u, w["w_down"])
 
     return dict(mod=mod, h1=h1, q=q.reshape(len(r), A), k=k.reshape(T, A), v=v.reshape(T, A),
                 o=o, x1=x1, h2=h2, u=u, out=out, rows=r)
