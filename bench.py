@@ -29,6 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 (MXFP8 scaled) MFMA: twice the bf16 rate
+GEMM_STAGES = ("qkv_rope_gemm", "out_proj_gemm", "mlp_up_gelu_gemm", "mlp_down_gemm")
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "DiT block tokens/s + TFLOP/s (% bf16 MFMA peak), 4096/16384 image tokens"
 
@@ -67,13 +69,13 @@ def block_flops(cfg) -> float:
     return 2.0 * T * (3 * A * D + A * D + 2 * D * F) + 4.0 * T * T * A + 2.0 * 6 * D * D
 
 
-def measure(cfg, steps: int, warmup: int):
+def measure(cfg, steps: int, warmup: int, linears: str = "bf16"):
     import torch
     from joint_attention_dit_amd import binding as B
     from joint_attention_dit_amd.inputs import make_inputs
 
     inp = make_inputs(cfg, seed=0)
-    blk = B.Block(cfg, inp, device="cuda:0")
+    blk = B.Block(cfg, inp, device="cuda:0", linears=linears)
     del inp
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -102,17 +104,20 @@ def measure(cfg, steps: int, warmup: int):
     return ms, stage_ms, out_ok
 
 
-def summarize(cfg, ms, stage_ms):
+def summarize(cfg, ms, stage_ms, linears: str = "bf16"):
     flops, nbytes = stage_work(cfg)
     total = block_flops(cfg)
     tflops = total / (ms * 1e-3) / 1e12
+    # each product kernel against the matrix-core peak of its own operand type
+    peak = {s: (PEAK_FP8_TFLOPS if linears == "mxfp8" and s in GEMM_STAGES else PEAK_BF16_TFLOPS)
+            for s in STAGES}
     kernels = {}
     for s in STAGES:
         t = stage_ms[s] * 1e-3
         k = {"ms": round(stage_ms[s], 4)}
         if s in flops and s != "modulation":
             k["tflops"] = round(flops[s] / t / 1e12, 1)
-            k["pct_mfma_peak"] = round(100 * flops[s] / t / 1e12 / PEAK_BF16_TFLOPS, 1)
+            k["pct_mfma_peak"] = round(100 * flops[s] / t / 1e12 / peak[s], 1)
         else:
             k["gbs"] = round(nbytes[s] / t / 1e9, 1)
             k["pct_hbm_peak"] = round(100 * nbytes[s] / t / 1e9 / PEAK_HBM_GBS, 1)
@@ -121,10 +126,11 @@ def summarize(cfg, ms, stage_ms):
     t = stage_ms[dom] * 1e-3
     if dom in flops and dom != "modulation":
         ach = flops[dom] / t / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(dom), "traffic_unit": "HBM bytes per launch",
-                "algorithmic_per_launch": flops[dom]}
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": peak[dom],
+                "unit": "TFLOP/s", "frac": round(ach / peak[dom], 4),
+                "traffic": measured_traffic(dom) if linears == "bf16" or dom not in GEMM_STAGES
+                else None,
+                "traffic_unit": "HBM bytes per launch", "algorithmic_per_launch": flops[dom]}
     else:
         ach = nbytes[dom] / t / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
@@ -410,6 +416,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="4096", choices=["2048", "4096", "edit", "nonsquare", "tiny"])
     ap.add_argument("--extra", default="2048", help="second workload reported under 'extra' ('none' to skip)")
+    ap.add_argument("--linears", default="bf16", choices=["bf16", "mxfp8"],
+                    help="the block's four linears in bf16 (default) or MXFP8 (OCP MX, E4M3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=384, help="query rows of the oracle sample")
     ap.add_argument("--stack", action="store_true",
@@ -471,8 +479,8 @@ def main():
             "pct_bf16_mfma_peak": round(100 * fl / sec / 1e12 / PEAK_BF16_TFLOPS, 2),
             "output_finite": ok}), flush=True)
         return
-    ms, stage_ms, ok = measure(cfg, args.steps, args.warmup)
-    tflops, kernels, roof = summarize(cfg, ms, stage_ms)
+    ms, stage_ms, ok = measure(cfg, args.steps, args.warmup, args.linears)
+    tflops, kernels, roof = summarize(cfg, ms, stage_ms, args.linears)
 
     rec = {
         "metric": METRIC,
@@ -485,7 +493,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.linears == "bf16" else "mxfp8 linears (e4m3 + e8m0/32), bf16 attention",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights)",
         "config": {"workload": cfg.description, "n_tokens": cfg.n_tokens,
                    "image_tokens": cfg.image_tokens, "text_tokens": cfg.text_tokens,
@@ -500,8 +508,9 @@ def main():
     }
     if args.extra not in ("", "none") and args.extra != args.workload:
         ecfg = CONFIGS[args.extra]
-        ems, est, eok = measure(ecfg, max(args.steps // 2, 1), max(args.warmup // 2, 1))
-        etf, ekern, eroof = summarize(ecfg, ems, est)
+        ems, est, eok = measure(ecfg, max(args.steps // 2, 1), max(args.warmup // 2, 1),
+                                args.linears)
+        etf, ekern, eroof = summarize(ecfg, ems, est, args.linears)
         rec["extra"] = {"workload": ecfg.description, "n_tokens": ecfg.n_tokens,
                         "ms_per_step": round(ems, 4), "value": round(ecfg.n_tokens / (ems * 1e-3), 1),
                         "unit": "block-tokens/s", "tflops": round(etf, 1),

@@ -112,6 +112,21 @@ int h3dit_block_forward_timed(const h3dit_config *cfg, const void *x, const floa
                               void *workspace, size_t workspace_bytes, void *stream,
                               void *const *events, int n_events);
 
+/* Where a block forward keeps its intermediate tensors in the workspace
+ * (byte offsets from the workspace start; host-only). After h3dit_block_forward
+ * (linears = 0) or h3dit_block_forward_mxfp8 (linears = 1) has completed, the
+ * workspace holds: mod (fp64 [6D]), table (fp32 [T, 64, 2] RoPE cos/sin), h
+ * (bf16 [T, D], the second normalisation's h2), qk (bf16 [T, 2A], q rotated
+ * and scaled, then k rotated), vt (bf16 [H, 128, Tp], V transposed, token t at
+ * column t with bits 2 and 3 exchanged, zero past T), o (bf16 [T, A]), x1
+ * (fp32 [T, D]) and u (bf16 [T, F]). For inspection and tests; the contents
+ * are only defined between forwards on the same workspace. */
+typedef struct {
+    size_t mod, table, h, qk, vt, o, x1, u;
+} h3dit_workspace_map;
+
+int h3dit_workspace_layout(const h3dit_config *cfg, int32_t linears, h3dit_workspace_map *map);
+
 /* ---------------------------------------------------------------------------
  * Stage entry points: the same kernels that h3dit_block_forward runs, one
  * step at a time, for per-step parity checks and profiling. Shapes come from
@@ -184,6 +199,77 @@ int h3dit_mlp_down_residual(const h3dit_config *cfg, const void *u, const void *
  * Requirements: M, N >= 1; K a positive multiple of 64. */
 int h3dit_linear_f32(const void *x, const void *w, int32_t M, int32_t N, int32_t K, float *y,
                      void *stream);
+
+/* ---------------------------------------------------------------------------
+ * MXFP8 linears (vLLM blog "H3-Image Day-0 Support", section Inference
+ * Optimizations: the DiT's linears run in MXFP8; element and block formats
+ * from the OCP 8-bit floating point and Microscaling definitions).
+ *
+ * An MXFP8 matrix [rows, K] (K a multiple of 128) is a pair:
+ *   codes  [rows, K] uint8, row-major: OCP FP8 E4M3 (bias 7, largest finite
+ *          448, S.1111.111 is NaN and is never produced);
+ *   scales h3dit_mxfp8_scale_bytes(rows, K) bytes of E8M0 exponents (byte
+ *          X + 127 means 2^X), one per 32 consecutive K of a row, grouped in
+ *          1 KB blocks: block (p, t) covers rows 256 p .. 256 p + 255 and K
+ *          128 t .. 128 t + 127 and starts at byte (p * K / 128 + t) * 1024;
+ *          inside it the scale of row 256 p + 16 b + r (b, r < 16) and of K
+ *          block kb (< 4) is byte (kb * 16 + r) * 16 + b. Rows of the last
+ *          block past `rows` hold byte 0.
+ * The value of element (i, k) is e4m3(codes[i, k]) * 2^(scale - 127).
+ *
+ * Quantisation (h3dit_mxfp8_quantize): X = floor(log2(max |v| of the 32-block))
+ * - 8, or -127 for an all-zero block; each element is v * 2^-X rounded to the
+ * nearest E4M3 value, ties to even, saturating at +-448, sign kept on zero.
+ * Inputs must be finite.
+ * ------------------------------------------------------------------------- */
+
+/* MXFP8 block weights (host struct of device pointers): each linear of
+ * h3dit_weights as codes + scales, quantised from the bf16 weight with
+ * h3dit_mxfp8_quantize ([out, in] rows, K = in). */
+typedef struct {
+    const uint8_t *w_qkv, *w_qkv_scale;   /* [3A, D] */
+    const uint8_t *w_o, *w_o_scale;       /* [D, A]  */
+    const uint8_t *w_up, *w_up_scale;     /* [F, D]  */
+    const uint8_t *w_down, *w_down_scale; /* [D, F]  */
+} h3dit_mxfp8_weights;
+
+/* Bytes of the scale array of an MXFP8 matrix [rows, K] (host-only):
+ * ceil(rows / 256) * 256 * K / 32; 0 if rows < 1 or K is not a positive
+ * multiple of 128. */
+size_t h3dit_mxfp8_scale_bytes(int64_t rows, int64_t K);
+
+/* codes + scales (layout above) of the bf16 matrix x [rows, K].
+ * rows in [1, 2^31), K a multiple of 128 in [128, 2^20]. */
+int h3dit_mxfp8_quantize(const void *x, int64_t rows, int64_t K, uint8_t *codes,
+                         uint8_t *scales, void *stream);
+
+/* y[M, N] fp32 = X . W^T for MXFP8 operands X [M, K] and W [N, K] (codes +
+ * scales as above), fp32 accumulation in the matrix cores' scaled E4M3
+ * product. N % 4 == 0, K a multiple of 128. */
+int h3dit_linear_mxfp8(const uint8_t *x_codes, const uint8_t *x_scales, const uint8_t *w_codes,
+                       const uint8_t *w_scales, int32_t M, int32_t N, int32_t K, float *y,
+                       void *stream);
+
+/* Workspace of h3dit_block_forward_mxfp8 for this shape (host-only). */
+int h3dit_workspace_size_mxfp8(const h3dit_config *cfg, size_t *bytes);
+
+/* h3dit_block_forward with the four linears in MXFP8: h1, o, h2 and u (the
+ * bf16 tensors of the bf16 path) are quantised along K just before their
+ * linear, and the weights come from q. w supplies only w_ada (its other
+ * pointers are not read). hidden and ffn must be multiples of 128. Attention,
+ * the normalisations, RoPE, GELU and the residuals are as in the bf16 path. */
+int h3dit_block_forward_mxfp8(const h3dit_config *cfg, const void *x, const float *cond,
+                              const h3dit_weights *w, const h3dit_mxfp8_weights *q,
+                              const int32_t *positions, float *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Same, recording the 10 events of h3dit_block_forward_timed (each linear's
+ * phase includes the quantisation of its input). */
+int h3dit_block_forward_mxfp8_timed(const h3dit_config *cfg, const void *x, const float *cond,
+                                    const h3dit_weights *w, const h3dit_mxfp8_weights *q,
+                                    const int32_t *positions, float *out, void *workspace,
+                                    size_t workspace_bytes, void *stream, void *const *events,
+                                    int n_events);
 
 /* ---------------------------------------------------------------------------
  * The DiT stack around the blocks (model card, "Model Architecture": latents

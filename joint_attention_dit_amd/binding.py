@@ -28,7 +28,9 @@ EXPORTED = (
     "h3dit_mlp_down_residual", "h3dit_linear_f32", "h3dit_stack_workspace_size",
     "h3dit_dit_forward", "h3dit_latent_step", "h3dit_padded_tokens", "h3dit_status_string",
     "h3dit_last_error", "h3dit_modulation_table", "h3dit_dit_modulation_table",
-    "h3dit_dit_forward_mod",
+    "h3dit_dit_forward_mod", "h3dit_mxfp8_scale_bytes", "h3dit_mxfp8_quantize",
+    "h3dit_linear_mxfp8", "h3dit_workspace_size_mxfp8", "h3dit_block_forward_mxfp8",
+    "h3dit_block_forward_mxfp8_timed", "h3dit_workspace_layout",
 )
 
 
@@ -49,6 +51,17 @@ class Weights(ctypes.Structure):
     _fields_ = [("w_ada", ctypes.c_void_p), ("w_qkv", ctypes.c_void_p),
                 ("w_o", ctypes.c_void_p), ("w_up", ctypes.c_void_p),
                 ("w_down", ctypes.c_void_p)]
+
+
+class MxWeights(ctypes.Structure):
+    _fields_ = [("w_qkv", ctypes.c_void_p), ("w_qkv_scale", ctypes.c_void_p),
+                ("w_o", ctypes.c_void_p), ("w_o_scale", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("w_up_scale", ctypes.c_void_p),
+                ("w_down", ctypes.c_void_p), ("w_down_scale", ctypes.c_void_p)]
+
+
+class WorkspaceMap(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("mod", "table", "h", "qk", "vt", "o", "x1", "u")]
 
 
 class StackConfig(ctypes.Structure):
@@ -98,11 +111,22 @@ def load_library() -> ctypes.CDLL:
                                        ctypes.POINTER(StackWeights), vp, ctypes.c_int, vp, vp],
         "h3dit_dit_forward_mod": [cfgp, ctypes.POINTER(StackConfig), ctypes.POINTER(StackWeights),
                                   vp, vp, vp, vp, vp, vp, sz, vp],
+        "h3dit_mxfp8_quantize": [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp],
+        "h3dit_linear_mxfp8": [vp, vp, vp, vp, i32, i32, i32, vp, vp],
+        "h3dit_workspace_size_mxfp8": [cfgp, ctypes.POINTER(sz)],
+        "h3dit_workspace_layout": [cfgp, i32, ctypes.POINTER(WorkspaceMap)],
+        "h3dit_block_forward_mxfp8": [cfgp, vp, vp, ctypes.POINTER(Weights),
+                                      ctypes.POINTER(MxWeights), vp, vp, vp, sz, vp],
+        "h3dit_block_forward_mxfp8_timed": [cfgp, vp, vp, ctypes.POINTER(Weights),
+                                            ctypes.POINTER(MxWeights), vp, vp, vp, sz, vp,
+                                            ctypes.POINTER(vp), ctypes.c_int],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.h3dit_mxfp8_scale_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    lib.h3dit_mxfp8_scale_bytes.restype = ctypes.c_size_t
     lib.h3dit_padded_tokens.argtypes = [ctypes.c_int64]
     lib.h3dit_padded_tokens.restype = ctypes.c_int64
     lib.h3dit_status_string.argtypes = [ctypes.c_int]
@@ -303,28 +327,144 @@ def h3dit_latent_step(latent: torch.Tensor, v: torch.Tensor, dt: float, stream=N
                                             _stream(stream)), "h3dit_latent_step")
 
 
+def h3dit_mxfp8_scale_bytes(rows: int, K: int) -> int:
+    return int(load_library().h3dit_mxfp8_scale_bytes(rows, K))
+
+
+def h3dit_mxfp8_quantize(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                         stream=None) -> None:
+    """bf16 x [rows, K] -> codes uint8 [rows, K] + scales uint8 (1 KB block layout)."""
+    rows, K = x.shape
+    _check(load_library().h3dit_mxfp8_quantize(_ptr(x), rows, K, _ptr(codes), _ptr(scales),
+                                               _stream(stream)), "h3dit_mxfp8_quantize")
+
+
+def h3dit_linear_mxfp8(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
+                       y: torch.Tensor, stream=None) -> None:
+    M, K = xq.shape
+    N = wq.shape[0]
+    _check(load_library().h3dit_linear_mxfp8(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K,
+                                             _ptr(y), _stream(stream)), "h3dit_linear_mxfp8")
+
+
+def h3dit_workspace_size_mxfp8(cfg: Config) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().h3dit_workspace_size_mxfp8(ctypes.byref(cfg), ctypes.byref(n)),
+           "h3dit_workspace_size_mxfp8")
+    return n.value
+
+
+def h3dit_workspace_layout(cfg: Config, linears: str = "bf16") -> WorkspaceMap:
+    m = WorkspaceMap()
+    _check(load_library().h3dit_workspace_layout(ctypes.byref(cfg), 1 if linears == "mxfp8" else 0,
+                                                 ctypes.byref(m)), "h3dit_workspace_layout")
+    return m
+
+
+def mxfp8_quantize(x: torch.Tensor, stream=None):
+    """Allocate and fill (codes, scales) for the bf16 matrix x [rows, K]."""
+    rows, K = x.shape
+    codes = torch.empty(rows, K, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(h3dit_mxfp8_scale_bytes(rows, K), dtype=torch.uint8, device=x.device)
+    h3dit_mxfp8_quantize(x, codes, scales, stream)
+    return codes, scales
+
+
+MX_LINEARS = ("w_qkv", "w_o", "w_up", "w_down")
+
+
+def mx_weights_struct(q: Dict[str, torch.Tensor]) -> MxWeights:
+    """q holds '<name>' codes and '<name>_scale' scales for each of MX_LINEARS."""
+    args = []
+    for k in MX_LINEARS:
+        args += [_ptr(q[k]), _ptr(q[k + "_scale"])]
+    return MxWeights(*args)
+
+
+def h3dit_block_forward_mxfp8(cfg: Config, x, cond, w, q, positions, out, workspace,
+                              stream=None) -> None:
+    ws, qs = weights_struct(w), mx_weights_struct(q)
+    _check(load_library().h3dit_block_forward_mxfp8(
+        ctypes.byref(cfg), _ptr(x), _ptr(cond), ctypes.byref(ws), ctypes.byref(qs),
+        _ptr(positions), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "h3dit_block_forward_mxfp8")
+
+
+def h3dit_block_forward_mxfp8_timed(cfg: Config, x, cond, w, q, positions, out, workspace,
+                                    events: Sequence[int], stream=None) -> None:
+    ws, qs = weights_struct(w), mx_weights_struct(q)
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(load_library().h3dit_block_forward_mxfp8_timed(
+        ctypes.byref(cfg), _ptr(x), _ptr(cond), ctypes.byref(ws), ctypes.byref(qs),
+        _ptr(positions), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream), arr, len(events)), "h3dit_block_forward_mxfp8_timed")
+
+
 # ------------------------------------------------------------------ helpers
 class Block:
     """Device-resident inputs + workspace for repeated h3dit_block_forward calls."""
 
-    def __init__(self, block_cfg, inputs: Dict[str, torch.Tensor], device: str = "cuda"):
+    def __init__(self, block_cfg, inputs: Dict[str, torch.Tensor], device: str = "cuda",
+                 linears: str = "bf16"):
+        """linears: "bf16", or "mxfp8" (weights quantised once here, on the GPU)."""
+        if linears not in ("bf16", "mxfp8"):
+            raise ValueError(f"linears must be 'bf16' or 'mxfp8' (got {linears!r})")
         self.block_cfg = block_cfg
         self.cfg = config_from(block_cfg)
+        self.linears = linears
         self.dev = {k: v.to(device).contiguous() for k, v in inputs.items()}
         self.weights = {k: self.dev[k] for k in ("w_ada", "w_qkv", "w_o", "w_up", "w_down")}
         T, D = block_cfg.n_tokens, block_cfg.hidden
         self.out = torch.empty(T, D, dtype=torch.float32, device=device)
-        nbytes = h3dit_workspace_size(self.cfg)
+        self.mx = None
+        if linears == "mxfp8":
+            self.mx = {}
+            for k in MX_LINEARS:
+                self.mx[k], self.mx[k + "_scale"] = mxfp8_quantize(self.weights[k])
+            nbytes = h3dit_workspace_size_mxfp8(self.cfg)
+        else:
+            nbytes = h3dit_workspace_size(self.cfg)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     def forward(self, stream=None) -> torch.Tensor:
         d = self.dev
-        h3dit_block_forward(self.cfg, d["x"], d["cond"], self.weights, d["positions"], self.out,
-                            self.workspace, stream)
+        if self.mx is not None:
+            h3dit_block_forward_mxfp8(self.cfg, d["x"], d["cond"], self.weights, self.mx,
+                                      d["positions"], self.out, self.workspace, stream)
+        else:
+            h3dit_block_forward(self.cfg, d["x"], d["cond"], self.weights, d["positions"],
+                                self.out, self.workspace, stream)
         return self.out
+
+    def intermediates(self) -> Dict[str, torch.Tensor]:
+        """Views of the intermediate tensors the last forward left in the workspace
+        (h3dit_workspace_layout): mod, table, h (= h2), qk, vt, o, x1, u."""
+        c = self.block_cfg
+        T, D, A, F, H = c.n_tokens, c.hidden, c.attn_width, c.ffn, c.heads
+        Tp = h3dit_padded_tokens(T)
+        m = h3dit_workspace_layout(self.cfg, self.linears)
+        ws = self.workspace
+
+        def view(off, n, dtype, shape):
+            nb = n * torch.tensor([], dtype=dtype).element_size()
+            return ws[off:off + nb].view(dtype).reshape(shape)
+
+        return {"mod": view(m.mod, 6 * D, torch.float64, (6 * D,)),
+                "table": view(m.table, T * 128, torch.float32, (T, 64, 2)),
+                "h": view(m.h, T * D, torch.bfloat16, (T, D)),
+                "qk": view(m.qk, T * 2 * A, torch.bfloat16, (T, 2 * A)),
+                "vt": view(m.vt, A * Tp, torch.bfloat16, (H, 128, Tp)),
+                "o": view(m.o, T * A, torch.bfloat16, (T, A)),
+                "x1": view(m.x1, T * D, torch.float32, (T, D)),
+                "u": view(m.u, T * F, torch.bfloat16, (T, F))}
 
     def forward_timed(self, events: Sequence[int], stream=None) -> torch.Tensor:
         d = self.dev
-        h3dit_block_forward_timed(self.cfg, d["x"], d["cond"], self.weights, d["positions"],
-                                  self.out, self.workspace, events, stream)
+        if self.mx is not None:
+            h3dit_block_forward_mxfp8_timed(self.cfg, d["x"], d["cond"], self.weights, self.mx,
+                                            d["positions"], self.out, self.workspace, events,
+                                            stream)
+        else:
+            h3dit_block_forward_timed(self.cfg, d["x"], d["cond"], self.weights, d["positions"],
+                                      self.out, self.workspace, events, stream)
         return self.out

@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh3dit.so")
 
 SOURCES = ["h3dit_api.cpp", "modulation.hip", "rmsnorm_modulate.hip", "rope_table.hip",
-           "gemm.hip", "attention.hip", "stack.hip"]
+           "gemm.hip", "gemm_mx.hip", "mxfp8.hip", "attention.hip", "stack.hip"]
 
 ARCH = "gfx950"
 CFLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -38,210 +38,17 @@
 // linear id is remapped so that each XCD receives a contiguous range of
 // tiles, and tiles are walked in groups of 8 token tiles so that the tiles
 // in flight on one XCD share weight and activation panels in its L2.
-#include "common.h"
-#include "kernels.h"
+#include "gemm_common.h"
 
-#include <algorithm>
 #include <type_traits>
 
 namespace h3dit {
 
 namespace {
 
-constexpr int BN = 256;   // weight rows (output features) per tile
-constexpr int BT = 256;   // activation rows (tokens) per tile
 constexpr int BK = 64;    // K per LDS stage (128-byte rows)
 constexpr int TILE_ELEMS = 256 * BK;  // one operand tile, bf16 elements (32 KB)
-constexpr int GROUP_T = 8;
 
-// LDS rows are 128 bytes (8 chunks of 16 B); 2 rows share one 256-byte bank line,
-// so chunk c of row r is stored at chunk c ^ ((r >> 1) & 7).
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-
-// Tile L of the grouped walk: GROUP_T token tiles per group, features outer
-// within the group.
-__device__ __forceinline__ void walk_coords(int L, int tiles_n, int tiles_t, int &tn, int &tt) {
-  const int per_group = GROUP_T * tiles_n;
-  const int g = L / per_group;
-  const int first_t = g * GROUP_T;
-  const int gt = min(tiles_t - first_t, GROUP_T);
-  const int in = L - g * per_group;
-  tt = first_t + in % gt;
-  tn = in / gt;
-}
-
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tiles_n, int tiles_t,
-                                            int &tn, int &tt) {
-  // XCD-contiguous remap (bijective for any nblocks)
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int q = nblocks >> 3, r = nblocks & 7;
-  const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
-  walk_coords(L, tiles_n, tiles_t, tn, tt);
-}
-
-// Split tiles: K slices of one tile are workgroups full_tiles + t * split + s;
-// slice s covers K tiles [s * per, min((s + 1) * per, ktiles)).
-__device__ __forceinline__ int slice_ktiles(int ktiles, int split) {
-  return (ktiles + split - 1) / split;
-}
-
-__device__ __forceinline__ float gelu_tanh(float z) {
-  // 0.5 z (1 + tanh(y)) == z / (1 + exp(-2y)),  y = sqrt(2/pi) (z + 0.044715 z^3)
-  const float y = 0.7978845608028654f * (z + 0.044715f * z * z * z);
-  return z / (1.0f + expf(-2.0f * y));
-}
-
-// q or k: rotate the two adjacent pairs of the fp32 products, then round once;
-// q also takes the softmax factor log2(e)/sqrt(128) before its rounding, so that
-// attention scores leave the matrix cores in base-2 units.
-__device__ __forceinline__ bf16x4 qk_rope4(const GemmArgs &a, int t, int n, float v0, float v1,
-                                           float v2, float v3) {
-  const float u0 = v0, w0 = v1, u1 = v2, w1 = v3;
-  const int p = (n & 127) >> 1;  // pair index within the head (0..63)
-  const f32x4 cs = *reinterpret_cast<const f32x4 *>(a.table + ((int64_t)t * 64 + p) * 2);
-  const float sc = n < a.A ? kLog2eOverSqrt128 : 1.0f;
-  bf16x4 r;
-  r[0] = to_bf16((u0 * cs[0] - w0 * cs[1]) * sc);
-  r[1] = to_bf16((u0 * cs[1] + w0 * cs[0]) * sc);
-  r[2] = to_bf16((u1 * cs[2] - w1 * cs[3]) * sc);
-  r[3] = to_bf16((u1 * cs[3] + w1 * cs[2]) * sc);
-  return r;
-}
-
-__device__ __forceinline__ bf16x4 gelu4(float v0, float v1, float v2, float v3) {
-  bf16x4 r;
-  r[0] = to_bf16(gelu_tanh(v0));
-  r[1] = to_bf16(gelu_tanh(v1));
-  r[2] = to_bf16(gelu_tanh(v2));
-  r[3] = to_bf16(gelu_tanh(v3));
-  return r;
-}
-
-// token t of a V tile is stored at column t with bits 2 and 3 exchanged (the key
-// order of the attention kernel's P V fragments)
-__device__ __forceinline__ int vt_col(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
-
-// Four consecutive outputs (features n .. n+3 of token t) through the epilogue.
-template <int EPI>
-__device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0, float v1,
-                                       float v2, float v3) {
-  if (n >= a.N) return;
-  if constexpr (EPI == EPI_QKV_ROPE) {
-    const int A2 = 2 * a.A;
-    if (n < A2) {
-      if (t >= a.M) return;
-      *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * A2 + n) =
-          qk_rope4(a, t, n, v0, v1, v2, v3);
-    } else {
-      if (t >= a.Mp) return;
-      const int hv = n - A2;  // head * 128 + dim
-      const int col = vt_col(t);
-      bf16 *vt = static_cast<bf16 *>(a.out2) + (int64_t)hv * a.Mp + col;
-      const bool live = t < a.M;
-      vt[0] = to_bf16(live ? v0 : 0.0f);
-      vt[a.Mp] = to_bf16(live ? v1 : 0.0f);
-      vt[2 * (int64_t)a.Mp] = to_bf16(live ? v2 : 0.0f);
-      vt[3 * (int64_t)a.Mp] = to_bf16(live ? v3 : 0.0f);
-    }
-  } else if constexpr (EPI == EPI_RESID_BF16 || EPI == EPI_RESID_F32) {
-    if (t >= a.M) return;
-    const int64_t off = (int64_t)t * a.N + n;
-    f32x4 rv;
-    if constexpr (EPI == EPI_RESID_BF16) {
-      const bf16x4 rb = *reinterpret_cast<const bf16x4 *>(static_cast<const bf16 *>(a.resid) + off);
-      rv = f32x4{(float)rb[0], (float)rb[1], (float)rb[2], (float)rb[3]};
-    } else {
-      rv = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.resid) + off);
-    }
-    f32x4 ov;
-    ov[0] = rv[0] + (float)a.gate[n + 0] * v0;
-    ov[1] = rv[1] + (float)a.gate[n + 1] * v1;
-    ov[2] = rv[2] + (float)a.gate[n + 2] * v2;
-    ov[3] = rv[3] + (float)a.gate[n + 3] * v3;
-    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + off) = ov;
-  } else if constexpr (EPI == EPI_F32) {
-    if (t >= a.M) return;
-    *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (int64_t)t * a.N + n) =
-        f32x4{v0, v1, v2, v3};
-  } else {  // EPI_GELU
-    if (t >= a.M) return;
-    *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * a.N + n) =
-        gelu4(v0, v1, v2, v3);
-  }
-}
-
-// bf16 staging of a 256 x 256 output tile in LDS (element offset): 16-byte chunk
-// c of row r sits at chunk c ^ (2 (r & 15)), so the 16 rows written by a fragment
-// block and the whole rows read back both spread over all banks.
-__device__ __forceinline__ int stage_off(int row, int col) {
-  return row * 256 + ((((col >> 3) ^ ((row & 15) << 1))) << 3) + (col & 7);
-}
-
-// bf16 epilogue through LDS: the wave's results go to the staged tile (tokens x
-// features for q/k; features x tokens, columns in the attention's key order, for
-// V), then every thread stores whole 16-byte chunks of rows, so each store
-// instruction writes two contiguous 512-byte rows (instead of 2-byte scattered
-// stores for V). Used for the QKV epilogue (about 1.5 % faster there); the
-// GELU epilogue's direct 8-byte stores are as fast.
-template <int EPI>
-__device__ __forceinline__ void staged_bf16_epilogue(const GemmArgs &a, bf16 *lds, const f32x4 (&acc)[8][4],
-                                                     int n0, int t0, int wn, int wt, int r16, int kq) {
-  const int tid = threadIdx.x;
-  bool vtile = false;
-  if constexpr (EPI == EPI_QKV_ROPE) vtile = n0 >= 2 * a.A;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tl = wt * 64 + 16 * j + r16, fl = wn * 128 + 16 * i + 4 * kq;
-      const int t = t0 + tl, n = n0 + fl;
-      const f32x4 v = acc[i][j];
-      if constexpr (EPI == EPI_QKV_ROPE) {
-        if (vtile) {
-          const bool live = t < a.M;
-          const int col = vt_col(tl);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lds[stage_off(fl + e, col)] = to_bf16(live ? v[e] : 0.0f);
-          continue;
-        }
-        const bf16x4 r = t < a.M ? qk_rope4(a, t, n, v[0], v[1], v[2], v[3]) : bf16x4{};
-        *reinterpret_cast<bf16x4 *>(lds + stage_off(tl, fl)) = r;
-      } else {
-        *reinterpret_cast<bf16x4 *>(lds + stage_off(tl, fl)) = gelu4(v[0], v[1], v[2], v[3]);
-      }
-    }
-  __syncthreads();
-#pragma unroll 4
-  for (int q = tid; q < 256 * 32; q += 512) {
-    const int row = q >> 5, c = q & 31;
-    const bf16x8 val = *reinterpret_cast<const bf16x8 *>(lds + stage_off(row, 8 * c));
-    if (vtile) {  // row = feature of the V tile, 8 tokens per chunk
-      const int hv = n0 - 2 * a.A + row, t = t0 + 8 * c;
-      if (hv < a.A && t < a.Mp)
-        *reinterpret_cast<bf16x8 *>(static_cast<bf16 *>(a.out2) + (int64_t)hv * a.Mp + t) = val;
-    } else {  // row = token, 8 features per chunk
-      const int t = t0 + row, n = n0 + 8 * c;
-      const int ld = EPI == EPI_QKV_ROPE ? 2 * a.A : a.N;
-      const int nend = EPI == EPI_QKV_ROPE ? 2 * a.A : a.N;
-      if (t < a.M && n < nend)
-        *reinterpret_cast<bf16x8 *>(static_cast<bf16 *>(a.out) + (int64_t)t * ld + n) = val;
-    }
-  }
-}
-
-// Wait until at most N of this wave's global-to-LDS copies are still in
-// flight (they complete in issue order), then meet the other waves: afterwards
-// every wave's earlier copies have landed in LDS. Instructions are not moved
-// across it in either direction.
-template <int N>
-__device__ __forceinline__ void tile_barrier() {
-  // s_waitcnt vmcnt(N) (lgkmcnt and expcnt fields left at their maximum)
-  constexpr int enc = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(enc);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
@@ -442,71 +249,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
                   acc[i][j][3]);
 }
 
-// Sum of the K slices of split tile full_tiles + blockIdx.x (in slice order),
-// then the epilogue, with the thread -> output mapping of gemm_kernel;
-// workgroup blockIdx.y takes feature blocks 2 y and 2 y + 1 of every wave.
-template <int EPI>
-__global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wt = wave >> 1;
-  const int r16 = lane & 15, kq = lane >> 4;
-  const int tiles_n = (int)ceil_div(a.N, BN), tiles_t = (int)ceil_div(a.M, BT);
-  int tn, tt;
-  walk_coords(a.full_tiles + blockIdx.x, tiles_n, tiles_t, tn, tt);
-  const f32x4 *src =
-      reinterpret_cast<const f32x4 *>(a.partial) + (int64_t)blockIdx.x * a.split * (32 * 512) + tid;
-  const int nb = tn * BN + wn * 128 + 4 * kq, tb = tt * BT + wt * 64 + r16;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * (int)blockIdx.y + ii;
-      const int64_t o = (i * 4 + j) * 512;
-      f32x4 v = src[o];
-      for (int sl = 1; sl < a.split; ++sl) v += src[(int64_t)sl * (32 * 512) + o];
-      store4<EPI>(a, tb + 16 * j, nb + 16 * i, v[0], v[1], v[2], v[3]);
-    }
-}
-
 }  // namespace
 
-// Compute units of the current device (cached per device).
-constexpr int kPlanCus = 256;  // MI355X; scratch is sized for it, larger devices split less
-static int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
-// One workgroup per CU at a time: when the last wave of tiles is at most half
-// full, its tiles are split along K into as many slices as fill the CUs (and
-// fit the scratch); a second kernel adds the slices. Returns the number of
-// slices per split tile (1: no split) and the number of split tiles.
-static int plan_split(int64_t M, int64_t N, int64_t K, int cus, size_t scratch_bytes, int *rem_out) {
-  const int tiles = (int)(ceil_div(N, BN) * ceil_div(M, BT));
-  const int ktiles = (int)(K / BK);
-  const int rem = tiles % cus;
-  *rem_out = 0;
-  if (rem == 0 || 2 * rem > cus || ktiles < 2) return 1;
-  const size_t piece_bytes = (size_t)BN * BT * 4;
-  const size_t fit = scratch_bytes / (piece_bytes * (size_t)rem);
-  const int split = (int)std::min<size_t>((size_t)std::min(cus / rem, ktiles), fit);
-  if (split < 2) return 1;
-  const int per = (ktiles + split - 1) / split;
-  *rem_out = rem;
-  return (ktiles + per - 1) / per;  // every slice non-empty
-}
 
 size_t gemm_split_scratch_bytes(int64_t M, int64_t N, int64_t K) {
   int rem = 0;
-  const int split = plan_split(M, N, K, kPlanCus, (size_t)-1, &rem);
+  const int split = plan_split(M, N, (int)(K / BK), kPlanCus, (size_t)-1, &rem);
   return split > 1 ? (size_t)rem * split * BN * BT * 4 : 0;
 }
 
@@ -515,7 +263,7 @@ static hipError_t launch_epi(const GemmArgs &a0, hipStream_t s) {
   GemmArgs a = a0;
   const int tiles = (int)(ceil_div(a.N, BN) * ceil_div(a.M, BT));
   int rem = 0;
-  a.split = a.partial ? plan_split(a.M, a.N, a.K, device_cus(), a.partial_bytes, &rem) : 1;
+  a.split = a.partial ? plan_split(a.M, a.N, a.K / BK, device_cus(), a.partial_bytes, &rem) : 1;
   a.full_tiles = tiles - (a.split > 1 ? rem : 0);
   const int grid = a.split > 1 ? a.full_tiles + rem * a.split : tiles;
   hipLaunchKernelGGL(gemm_kernel<EPI>, dim3(grid), dim3(512), 0, s, a);

@@ -91,11 +91,16 @@ int check_config(const h3dit_config *cfg) {
 struct Plan {
   int64_t T, D, A, H, F, Tp;
   size_t mod, table, h, qk, vt, o, x1, u, split, split_bytes, total;
+  size_t q, qs;  // MXFP8: codes and scales of the linear's input (one at a time)
 };
+
+size_t mx_scale_bytes(int64_t rows, int64_t K) {
+  return (size_t)((rows + 255) / 256) * 256 * (size_t)(K / 32);
+}
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-Plan make_plan(const h3dit_config *c) {
+Plan make_plan(const h3dit_config *c, bool mx = false) {
   Plan p;
   p.T = c->n_tokens;
   p.D = c->hidden;
@@ -118,11 +123,16 @@ Plan make_plan(const h3dit_config *c) {
   p.x1 = take(4 * p.T * p.D);
   p.u = take(2 * p.T * p.F);
   // K slices of the four GEMMs' last waves (one GEMM at a time)
-  p.split_bytes = std::max(std::max(gemm_split_scratch_bytes(p.T, 3 * p.A, p.D),
-                                    gemm_split_scratch_bytes(p.T, p.D, p.A)),
-                           std::max(gemm_split_scratch_bytes(p.T, p.F, p.D),
-                                    gemm_split_scratch_bytes(p.T, p.D, p.F)));
+  auto split_bytes = mx ? gemm_mx_split_scratch_bytes : gemm_split_scratch_bytes;
+  p.split_bytes = std::max(std::max(split_bytes(p.T, 3 * p.A, p.D), split_bytes(p.T, p.D, p.A)),
+                           std::max(split_bytes(p.T, p.F, p.D), split_bytes(p.T, p.D, p.F)));
   p.split = take(p.split_bytes);
+  p.q = p.qs = 0;
+  if (mx) {
+    const int64_t kmax = std::max(std::max(p.D, p.A), p.F);
+    p.q = take((size_t)(p.T * kmax));
+    p.qs = take(mx_scale_bytes(p.T, kmax));
+  }
   p.total = off;
   return p;
 }
@@ -145,9 +155,12 @@ GemmArgs gemm_args(const void *x, const void *w, int64_t M, int64_t N, int64_t K
 
 // mod_in: the block's modulation (fp64 [6D]) computed beforehand, or NULL to
 // compute it from cond and w->w_ada.
+// q: MXFP8 weights (the four linears in MXFP8; w's linear weights unused), or
+// NULL for the bf16 linears.
 int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, const h3dit_weights *w,
                  const int32_t *positions, float *out, void *ws, size_t ws_bytes, void *stream,
-                 void *const *events, int n_events, const double *mod_in = nullptr) {
+                 void *const *events, int n_events, const double *mod_in = nullptr,
+                 const h3dit_mxfp8_weights *q = nullptr) {
   CHECK_CFG(cfg);
   if (!w) return fail(H3DIT_EINVAL, "w is NULL");
   CHECK_PTR(x);
@@ -158,16 +171,30 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     CHECK_PTR(cond);
     CHECK_PTR(w->w_ada);
   }
-  CHECK_PTR(w->w_qkv);
-  CHECK_PTR(w->w_o);
-  CHECK_PTR(w->w_up);
-  CHECK_PTR(w->w_down);
+  if (q) {
+    if (cfg->hidden % 128 != 0 || cfg->ffn % 128 != 0)
+      return fail(H3DIT_EUNSUPPORTED, "MXFP8 linears need hidden and ffn multiples of 128 "
+                  "(got %d, %d)", cfg->hidden, cfg->ffn);
+    CHECK_PTR(q->w_qkv);
+    CHECK_PTR(q->w_qkv_scale);
+    CHECK_PTR(q->w_o);
+    CHECK_PTR(q->w_o_scale);
+    CHECK_PTR(q->w_up);
+    CHECK_PTR(q->w_up_scale);
+    CHECK_PTR(q->w_down);
+    CHECK_PTR(q->w_down_scale);
+  } else {
+    CHECK_PTR(w->w_qkv);
+    CHECK_PTR(w->w_o);
+    CHECK_PTR(w->w_up);
+    CHECK_PTR(w->w_down);
+  }
   if (events) {
     if (n_events != 10) return fail(H3DIT_EINVAL, "n_events must be 10 (got %d)", n_events);
     for (int i = 0; i < 10; ++i)
       if (!events[i]) return fail(H3DIT_EINVAL, "events[%d] is NULL", i);
   }
-  const Plan p = make_plan(cfg);
+  const Plan p = make_plan(cfg, q != nullptr);
   if (ws_bytes < p.total)
     return fail(H3DIT_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.total);
   {
@@ -195,6 +222,22 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     if (!events) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
   };
+  // one linear: bf16 operands, or (MXFP8) the input quantised along K and the
+  // MXFP8 weight wq / wqs
+  uint8_t *qx = at<uint8_t>(ws, p.q), *qxs = at<uint8_t>(ws, p.qs);
+  auto linear = [&](GemmEpilogue epi, GemmArgs g, const uint8_t *wq,
+                    const uint8_t *wqs) -> hipError_t {
+    g.partial = split;
+    g.partial_bytes = p.split_bytes;
+    if (!q) return launch_gemm(epi, g, s);
+    const hipError_t e = launch_mxfp8_quantize(g.x, g.M, g.K, qx, qxs, s);
+    if (e != hipSuccess) return e;
+    g.x = qx;
+    g.x_scale = qxs;
+    g.w = wq;
+    g.w_scale = wqs;
+    return launch_gemm_mx(epi, g, s);
+  };
 
   LAUNCH(mark(0), "event record");
   if (!mod_in)
@@ -213,9 +256,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.table = table;
     g.A = A;
     g.Mp = (int)p.Tp;
-    g.partial = split;
-    g.partial_bytes = p.split_bytes;
-    LAUNCH(launch_gemm(EPI_QKV_ROPE, g, s), "qkv gemm");
+    LAUNCH(linear(EPI_QKV_ROPE, g, q ? q->w_qkv : nullptr, q ? q->w_qkv_scale : nullptr),
+           "qkv gemm");
   }
   LAUNCH(mark(4), "event record");
   LAUNCH(launch_attention(qk, vt, o, T, H, (int)p.Tp, s), "attention");
@@ -225,9 +267,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.out = x1;
     g.resid = x;
     g.gate = mod + 2 * D;
-    g.partial = split;
-    g.partial_bytes = p.split_bytes;
-    LAUNCH(launch_gemm(cfg->x_dtype == H3DIT_F32 ? EPI_RESID_F32 : EPI_RESID_BF16, g, s),
+    LAUNCH(linear(cfg->x_dtype == H3DIT_F32 ? EPI_RESID_F32 : EPI_RESID_BF16, g,
+                  q ? q->w_o : nullptr, q ? q->w_o_scale : nullptr),
            "output projection");
   }
   LAUNCH(mark(6), "event record");
@@ -237,9 +278,7 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   {
     GemmArgs g = gemm_args(h, w->w_up, T, F, D);
     g.out = u;
-    g.partial = split;
-    g.partial_bytes = p.split_bytes;
-    LAUNCH(launch_gemm(EPI_GELU, g, s), "mlp up");
+    LAUNCH(linear(EPI_GELU, g, q ? q->w_up : nullptr, q ? q->w_up_scale : nullptr), "mlp up");
   }
   LAUNCH(mark(8), "event record");
   {
@@ -247,9 +286,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.out = out;
     g.resid = x1;
     g.gate = mod + 5 * D;
-    g.partial = split;
-    g.partial_bytes = p.split_bytes;
-    LAUNCH(launch_gemm(EPI_RESID_F32, g, s), "mlp down");
+    LAUNCH(linear(EPI_RESID_F32, g, q ? q->w_down : nullptr, q ? q->w_down_scale : nullptr),
+           "mlp down");
   }
   LAUNCH(mark(9), "event record");
   return ok();
@@ -457,6 +495,23 @@ int h3dit_latent_step(float *latent, const float *v, float dt, int64_t n, void *
 
 int64_t h3dit_padded_tokens(int64_t n_tokens) { return (n_tokens + 63) / 64 * 64; }
 
+int h3dit_workspace_layout(const h3dit_config *cfg, int32_t linears, h3dit_workspace_map *map) {
+  CHECK_CFG(cfg);
+  if (!map) return fail(H3DIT_EINVAL, "map is NULL");
+  if (linears != 0 && linears != 1)
+    return fail(H3DIT_EINVAL, "linears must be 0 (bf16) or 1 (MXFP8) (got %d)", linears);
+  const Plan p = make_plan(cfg, linears == 1);
+  map->mod = p.mod;
+  map->table = p.table;
+  map->h = p.h;
+  map->qk = p.qk;
+  map->vt = p.vt;
+  map->o = p.o;
+  map->x1 = p.x1;
+  map->u = p.u;
+  return ok();
+}
+
 int h3dit_workspace_size(const h3dit_config *cfg, size_t *bytes) {
   CHECK_CFG(cfg);
   if (!bytes) return fail(H3DIT_EINVAL, "bytes is NULL");
@@ -624,6 +679,71 @@ int h3dit_linear_f32(const void *x, const void *w, int32_t M, int32_t N, int32_t
   g.out = y;
   LAUNCH(launch_gemm(EPI_F32, g, static_cast<hipStream_t>(stream)), "linear");
   return ok();
+}
+
+size_t h3dit_mxfp8_scale_bytes(int64_t rows, int64_t K) {
+  if (rows < 1 || K < 128 || K % 128 != 0) return 0;
+  return mx_scale_bytes(rows, K);
+}
+
+int h3dit_mxfp8_quantize(const void *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales,
+                         void *stream) {
+  CHECK_PTR(x);
+  CHECK_PTR(codes);
+  CHECK_PTR(scales);
+  if (rows < 1 || rows >= ((int64_t)1 << 31) || K < 128 || K % 128 != 0 || K > (1 << 20))
+    return fail(H3DIT_EUNSUPPORTED, "mxfp8 quantize: need rows in [1, 2^31) and K a multiple of "
+                "128 in [128, 2^20] (got rows=%lld K=%lld)", (long long)rows, (long long)K);
+  LAUNCH(launch_mxfp8_quantize(x, (int)rows, (int)K, codes, scales,
+                               static_cast<hipStream_t>(stream)),
+         "mxfp8 quantize");
+  return ok();
+}
+
+int h3dit_linear_mxfp8(const uint8_t *x_codes, const uint8_t *x_scales, const uint8_t *w_codes,
+                       const uint8_t *w_scales, int32_t M, int32_t N, int32_t K, float *y,
+                       void *stream) {
+  CHECK_PTR(x_codes);
+  CHECK_PTR(x_scales);
+  CHECK_PTR(w_codes);
+  CHECK_PTR(w_scales);
+  CHECK_PTR(y);
+  if (M < 1 || N < 1 || N % 4 != 0 || K < 128 || K % 128 != 0 || K > (1 << 20))
+    return fail(H3DIT_EUNSUPPORTED, "mxfp8 linear: need M, N >= 1, N %% 4 == 0, K a multiple of "
+                "128 (got M=%d N=%d K=%d)", M, N, K);
+  GemmArgs g = gemm_args(x_codes, w_codes, M, N, K);
+  g.x_scale = x_scales;
+  g.w_scale = w_scales;
+  g.out = y;
+  LAUNCH(launch_gemm_mx(EPI_F32, g, static_cast<hipStream_t>(stream)), "mxfp8 linear");
+  return ok();
+}
+
+int h3dit_workspace_size_mxfp8(const h3dit_config *cfg, size_t *bytes) {
+  CHECK_CFG(cfg);
+  if (!bytes) return fail(H3DIT_EINVAL, "bytes is NULL");
+  *bytes = make_plan(cfg, true).total;
+  return ok();
+}
+
+int h3dit_block_forward_mxfp8(const h3dit_config *cfg, const void *x, const float *cond,
+                              const h3dit_weights *w, const h3dit_mxfp8_weights *q,
+                              const int32_t *positions, float *out, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  if (!q) return fail(H3DIT_EINVAL, "q is NULL");
+  return forward_impl(cfg, x, cond, w, positions, out, workspace, workspace_bytes, stream, nullptr,
+                      0, nullptr, q);
+}
+
+int h3dit_block_forward_mxfp8_timed(const h3dit_config *cfg, const void *x, const float *cond,
+                                    const h3dit_weights *w, const h3dit_mxfp8_weights *q,
+                                    const int32_t *positions, float *out, void *workspace,
+                                    size_t workspace_bytes, void *stream, void *const *events,
+                                    int n_events) {
+  if (!q) return fail(H3DIT_EINVAL, "q is NULL");
+  if (!events) return fail(H3DIT_EINVAL, "events is NULL");
+  return forward_impl(cfg, x, cond, w, positions, out, workspace, workspace_bytes, stream, events,
+                      n_events, nullptr, q);
 }
 
 const char *h3dit_status_string(int status) {

@@ -32,8 +32,10 @@ hipError_t launch_rope_table(const int32_t *pos, float *table, int T, float base
 enum GemmEpilogue { EPI_QKV_ROPE = 0, EPI_RESID_BF16 = 1, EPI_RESID_F32 = 2, EPI_GELU = 3, EPI_F32 = 4 };
 
 struct GemmArgs {
-  const void *x;      // B operand rows: activations [M, K] bf16
-  const void *w;      // A operand rows: weights [N, K] bf16
+  const void *x;      // B operand rows: activations [M, K] bf16 (MXFP8: E4M3 codes)
+  const void *w;      // A operand rows: weights [N, K] bf16 (MXFP8: E4M3 codes)
+  const uint8_t *x_scale;  // MXFP8 only: E8M0 scales of x and w in the 1 KB
+  const uint8_t *w_scale;  // block layout of launch_mxfp8_quantize
   int M, N, K;
   // epilogue operands
   void *out;          // QKV: qk [M, 2A]; RESID, F32: fp32 [M, N]; GELU: bf16 [M, N]
@@ -59,6 +61,16 @@ hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s);
 // Scratch bytes that let launch_gemm split the last wave of an M x N x K GEMM
 // on a 256-CU device (0: it would not split).
 size_t gemm_split_scratch_bytes(int64_t M, int64_t N, int64_t K);
+
+// The same GEMM with MXFP8 operands (E4M3 codes, one E8M0 scale per 32 along
+// K); K % 128 == 0. Same epilogues, split and fixup as launch_gemm.
+hipError_t launch_gemm_mx(GemmEpilogue epi, const GemmArgs &a, hipStream_t s);
+size_t gemm_mx_split_scratch_bytes(int64_t M, int64_t N, int64_t K);
+
+// codes [rows, K] + scales (1 KB per 256-row panel and 128-wide K tile) from
+// bf16 x [rows, K]; K % 128 == 0
+hipError_t launch_mxfp8_quantize(const void *x, int rows, int K, uint8_t *codes, uint8_t *scales,
+                                 hipStream_t s);
 
 // o[T, A] = attention over qk [T, 2A] and vt [H, 128, Tp]
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,

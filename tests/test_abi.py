@@ -235,3 +235,58 @@ def test_dit_modulation_table_and_forward_mod_validation(lib):
     assert "mods" in lib.h3dit_last_error().decode()
     assert fwd(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), *args, 0xb00000000,
                0x800000000, 0x900000000, 0xa00000000, 4096, None) == B.H3DIT_EWORKSPACE
+
+
+# ------------------------------------------------------------------ MXFP8
+def test_mxfp8_struct_and_scale_bytes():
+    assert ctypes.sizeof(B.MxWeights) == 64
+    assert B.h3dit_mxfp8_scale_bytes(300, 384) == 512 * 12
+    assert B.h3dit_mxfp8_scale_bytes(256, 128) == 1024
+    assert B.h3dit_mxfp8_scale_bytes(16896, 14336) == 16896 * 448
+    for rows, K in ((0, 128), (10, 100), (10, 0), (-1, 256)):
+        assert B.h3dit_mxfp8_scale_bytes(rows, K) == 0
+
+
+def test_mxfp8_workspace_adds_quantised_operand():
+    cfg = full_cfg()
+    T, D, A, F = 16896, 5376, 7168, 14336
+    bf = B.h3dit_workspace_size(cfg)
+    mx = B.h3dit_workspace_size_mxfp8(cfg)
+    # codes and scales of the widest linear input (u, [T, F]); the split scratch
+    # follows the MXFP8 GEMM's 128-wide K tiles
+    assert mx - bf >= T * F + T * F // 32 - 112 * 2 * 256 * 256 * 4
+
+
+def test_mxfp8_quantize_and_linear_validation(lib):
+    x, c, s = P["x"], P["h"], P["mod"]
+    assert lib.h3dit_mxfp8_quantize(x, 10, 100, c, s, None) == B.H3DIT_EUNSUPPORTED
+    assert lib.h3dit_mxfp8_quantize(x, 0, 128, c, s, None) == B.H3DIT_EUNSUPPORTED
+    assert lib.h3dit_mxfp8_quantize(x, 10, 128, None, s, None) == B.H3DIT_EINVAL
+    assert lib.h3dit_mxfp8_quantize(x, 10, 128, c, s + 8, None) == B.H3DIT_EALIGN
+    y = P["out"]
+    assert lib.h3dit_linear_mxfp8(x, s, c, s, 4, 8, 192, y, None) == B.H3DIT_EUNSUPPORTED
+    assert lib.h3dit_linear_mxfp8(x, s, c, s, 4, 6, 128, y, None) == B.H3DIT_EUNSUPPORTED
+    assert lib.h3dit_linear_mxfp8(x, None, c, s, 4, 8, 128, y, None) == B.H3DIT_EINVAL
+
+
+def _forward_mx(lib, cfg, q=None, ws_bytes=1 << 40):
+    w = B.Weights(P["w_ada"], 0, 0, 0, 0)  # the bf16 linear weights are not read
+    if q is None:
+        q = B.MxWeights(*[0x200000000 * (i + 20) for i in range(8)])
+    return lib.h3dit_block_forward_mxfp8(ctypes.byref(cfg), P["x"], P["cond"], ctypes.byref(w),
+                                         ctypes.byref(q) if q is not False else None, P["pos"],
+                                         P["out"], P["ws"], ws_bytes, None)
+
+
+def test_mxfp8_forward_validation(lib):
+    with_fault = os.environ.get("H3DIT_FAULT_INJECT")
+    assert with_fault is None
+    assert _forward_mx(lib, full_cfg(), q=False) == B.H3DIT_EINVAL
+    assert _forward_mx(lib, full_cfg(hidden=5312)) == B.H3DIT_EUNSUPPORTED  # 83 * 64
+    assert "multiples of 128" in lib.h3dit_last_error().decode()
+    assert _forward_mx(lib, full_cfg(ffn=14400)) == B.H3DIT_EUNSUPPORTED
+    q = B.MxWeights(*[0x200000000 * (i + 20) for i in range(8)])
+    q.w_down_scale = None
+    assert _forward_mx(lib, full_cfg(), q=q) == B.H3DIT_EINVAL
+    need = B.h3dit_workspace_size_mxfp8(full_cfg())
+    assert _forward_mx(lib, full_cfg(), ws_bytes=need - 1) == B.H3DIT_EWORKSPACE
