@@ -123,6 +123,9 @@ int h3dit_block_forward_timed(const h3dit_config *cfg, const void *x, const floa
  * are only defined between forwards on the same workspace. */
 typedef struct {
     size_t mod, table, h, qk, vt, o, x1, u;
+    /* MXFP8 forward only (0 otherwise): h2 and u as MXFP8 codes ([T, D] and
+     * [T, F]) and their scales, in the layout of h3dit_mxfp8_quantize */
+    size_t q_h2, q_h2_scale, q_u, q_u_scale;
 } h3dit_workspace_map;
 
 int h3dit_workspace_layout(const h3dit_config *cfg, int32_t linears, h3dit_workspace_map *map);

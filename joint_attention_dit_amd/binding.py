@@ -61,7 +61,8 @@ class MxWeights(ctypes.Structure):
 
 
 class WorkspaceMap(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("mod", "table", "h", "qk", "vt", "o", "x1", "u")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("mod", "table", "h", "qk", "vt", "o", "x1", "u",
+                                                "q_h2", "q_h2_scale", "q_u", "q_u_scale")]
 
 
 class StackConfig(ctypes.Structure):
@@ -449,7 +450,14 @@ class Block:
             nb = n * torch.tensor([], dtype=dtype).element_size()
             return ws[off:off + nb].view(dtype).reshape(shape)
 
-        return {"mod": view(m.mod, 6 * D, torch.float64, (6 * D,)),
+        out = {}
+        if self.linears == "mxfp8":
+            sd, sf = h3dit_mxfp8_scale_bytes(T, D), h3dit_mxfp8_scale_bytes(T, F)
+            out.update({"q_h2": view(m.q_h2, T * D, torch.uint8, (T, D)),
+                        "q_h2_scale": view(m.q_h2_scale, sd, torch.uint8, (sd,)),
+                        "q_u": view(m.q_u, T * F, torch.uint8, (T, F)),
+                        "q_u_scale": view(m.q_u_scale, sf, torch.uint8, (sf,))})
+        return {**out, "mod": view(m.mod, 6 * D, torch.float64, (6 * D,)),
                 "table": view(m.table, T * 128, torch.float32, (T, 64, 2)),
                 "h": view(m.h, T * D, torch.bfloat16, (T, D)),
                 "qk": view(m.qk, T * 2 * A, torch.bfloat16, (T, 2 * A)),

@@ -280,6 +280,7 @@ hipError_t launch_gemm(GemmEpilogue epi, const GemmArgs &a, hipStream_t s) {
     case EPI_RESID_F32: return launch_epi<EPI_RESID_F32>(a, s);
     case EPI_GELU: return launch_epi<EPI_GELU>(a, s);
     case EPI_F32: return launch_epi<EPI_F32>(a, s);
+    case EPI_GELU_MX: return hipErrorInvalidValue;  // MXFP8 GEMM only
   }
   return hipErrorInvalidValue;
 }

@@ -7,6 +7,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mxfp8_device.h"
 
 #include <algorithm>
 
@@ -134,6 +135,40 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
   }
 }
 
+// GELU outputs of one block of 32 features of token t as bf16 (u) and as
+// MXFP8 codes + scale. The calling lane holds features n .. n + 3 (v0) and
+// n + 16 .. n + 19 (v1) with n = 32 m + 4 kq (kq = lane bits 4, 5); the four
+// lanes kq = 0..3 together hold the block, so every lane of the wave must
+// call this (the block maximum is exchanged across them). N % 32 == 0.
+__device__ __forceinline__ void gelu_mx_block(const GemmArgs &a, int t, int n, int kq,
+                                              const f32x4 &v0, const f32x4 &v1) {
+  const bf16x4 g0 = gelu4(v0[0], v0[1], v0[2], v0[3]);
+  const bf16x4 g1 = gelu4(v1[0], v1[1], v1[2], v1[3]);
+  // magnitudes of the eight bf16 values from whole-vector bit patterns (a
+  // bit cast of single vector elements kept only element 0 here)
+  const u32x2 w0 = __builtin_bit_cast(u32x2, g0), w1 = __builtin_bit_cast(u32x2, g1);
+  uint32_t amax = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    amax = max(amax, max(w0[e] & 0x7FFFu, (w0[e] >> 16) & 0x7FFFu));
+    amax = max(amax, max(w1[e] & 0x7FFFu, (w1[e] >> 16) & 0x7FFFu));
+  }
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16));
+  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+  const int sbyte = mx_scale_byte(amax);
+  const float inv = mx_inv_scale(sbyte);
+  if (t >= a.M || n >= a.N) return;
+  const int64_t off = (int64_t)t * a.N + n;
+  bf16 *u = static_cast<bf16 *>(a.out);
+  *reinterpret_cast<bf16x4 *>(u + off) = g0;
+  *reinterpret_cast<bf16x4 *>(u + off + 16) = g1;
+  *reinterpret_cast<uint32_t *>(a.out_codes + off) =
+      mx_code4((float)g0[0], (float)g0[1], (float)g0[2], (float)g0[3], inv);
+  *reinterpret_cast<uint32_t *>(a.out_codes + off + 16) =
+      mx_code4((float)g1[0], (float)g1[1], (float)g1[2], (float)g1[3], inv);
+  if (kq == 0) a.out_scales[mx_scale_offset(t, n >> 5, a.N)] = (uint8_t)sbyte;
+}
+
 // bf16 staging of a 256 x 256 output tile in LDS (element offset): 16-byte chunk
 // c of row r sits at chunk c ^ (2 (r & 15)), so the 16 rows written by a fragment
 // block and the whole rows read back both spread over all banks.
@@ -221,6 +256,20 @@ __global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
   const f32x4 *src =
       reinterpret_cast<const f32x4 *>(a.partial) + (int64_t)blockIdx.x * a.split * (32 * 512) + tid;
   const int nb = tn * BN + wn * 128 + 4 * kq, tb = tt * BT + wt * 64 + r16;
+  if constexpr (EPI == EPI_GELU_MX) {  // feature blocks 2 y, 2 y + 1 are one block of 32
+    const int i = 2 * (int)blockIdx.y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t o0 = (i * 4 + j) * 512, o1 = ((i + 1) * 4 + j) * 512;
+      f32x4 v0 = src[o0], v1 = src[o1];
+      for (int sl = 1; sl < a.split; ++sl) {
+        v0 += src[(int64_t)sl * (32 * 512) + o0];
+        v1 += src[(int64_t)sl * (32 * 512) + o1];
+      }
+      gelu_mx_block(a, tb + 16 * j, nb + 16 * i, kq, v0, v1);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll

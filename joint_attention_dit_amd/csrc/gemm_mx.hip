@@ -288,6 +288,14 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a) {
     return;
   }
   const int nb = n0 + wn * 128 + 4 * kq, tb = t0 + wt * 64 + r16;
+  if constexpr (EPI == EPI_GELU_MX) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        gelu_mx_block(a, tb + 16 * j, nb + 32 * m, kq, acc[2 * m][j], acc[2 * m + 1][j]);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -326,6 +334,7 @@ hipError_t launch_gemm_mx(GemmEpilogue epi, const GemmArgs &a, hipStream_t s) {
     case EPI_RESID_F32: return launch_mx_epi<EPI_RESID_F32>(a, s);
     case EPI_GELU: return launch_mx_epi<EPI_GELU>(a, s);
     case EPI_F32: return launch_mx_epi<EPI_F32>(a, s);
+    case EPI_GELU_MX: return launch_mx_epi<EPI_GELU_MX>(a, s);
   }
   return hipErrorInvalidValue;
 }

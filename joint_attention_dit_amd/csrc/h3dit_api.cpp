@@ -91,7 +91,9 @@ int check_config(const h3dit_config *cfg) {
 struct Plan {
   int64_t T, D, A, H, F, Tp;
   size_t mod, table, h, qk, vt, o, x1, u, split, split_bytes, total;
-  size_t q, qs;  // MXFP8: codes and scales of the linear's input (one at a time)
+  // MXFP8: codes and scales of the linears' inputs: region a holds h1, then o,
+  // then h2; region b holds u (written while h2's codes are being read)
+  size_t qa, qas, qb, qbs;
 };
 
 size_t mx_scale_bytes(int64_t rows, int64_t K) {
@@ -127,11 +129,13 @@ Plan make_plan(const h3dit_config *c, bool mx = false) {
   p.split_bytes = std::max(std::max(split_bytes(p.T, 3 * p.A, p.D), split_bytes(p.T, p.D, p.A)),
                            std::max(split_bytes(p.T, p.F, p.D), split_bytes(p.T, p.D, p.F)));
   p.split = take(p.split_bytes);
-  p.q = p.qs = 0;
+  p.qa = p.qas = p.qb = p.qbs = 0;
   if (mx) {
-    const int64_t kmax = std::max(std::max(p.D, p.A), p.F);
-    p.q = take((size_t)(p.T * kmax));
-    p.qs = take(mx_scale_bytes(p.T, kmax));
+    const int64_t ka = std::max(p.D, p.A);
+    p.qa = take((size_t)(p.T * ka));
+    p.qas = take(mx_scale_bytes(p.T, ka));
+    p.qb = take((size_t)(p.T * p.F));
+    p.qbs = take(mx_scale_bytes(p.T, p.F));
   }
   p.total = off;
   return p;
@@ -222,18 +226,22 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     if (!events) return hipSuccess;
     return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
   };
-  // one linear: bf16 operands, or (MXFP8) the input quantised along K and the
-  // MXFP8 weight wq / wqs
-  uint8_t *qx = at<uint8_t>(ws, p.q), *qxs = at<uint8_t>(ws, p.qs);
-  auto linear = [&](GemmEpilogue epi, GemmArgs g, const uint8_t *wq,
-                    const uint8_t *wqs) -> hipError_t {
+  // one linear: bf16 operands, or (MXFP8) the input's codes xq / xqs (written
+  // by its producer, or quantised here when quantise is set) and the MXFP8
+  // weight wq / wqs
+  uint8_t *qa = at<uint8_t>(ws, p.qa), *qas = at<uint8_t>(ws, p.qas);
+  uint8_t *qb = at<uint8_t>(ws, p.qb), *qbs = at<uint8_t>(ws, p.qbs);
+  auto linear = [&](GemmEpilogue epi, GemmArgs g, const uint8_t *wq, const uint8_t *wqs,
+                    uint8_t *xq, uint8_t *xqs, bool quantise) -> hipError_t {
     g.partial = split;
     g.partial_bytes = p.split_bytes;
     if (!q) return launch_gemm(epi, g, s);
-    const hipError_t e = launch_mxfp8_quantize(g.x, g.M, g.K, qx, qxs, s);
-    if (e != hipSuccess) return e;
-    g.x = qx;
-    g.x_scale = qxs;
+    if (quantise) {
+      const hipError_t e = launch_mxfp8_quantize(g.x, g.M, g.K, xq, xqs, s);
+      if (e != hipSuccess) return e;
+    }
+    g.x = xq;
+    g.x_scale = xqs;
     g.w = wq;
     g.w_scale = wqs;
     return launch_gemm_mx(epi, g, s);
@@ -245,9 +253,14 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   LAUNCH(mark(1), "event record");
   LAUNCH(launch_rope_table(positions, table, T, cfg->rope_base, s), "rope table");
   LAUNCH(mark(2), "event record");
-  LAUNCH(launch_rmsnorm_modulate(x, cfg->x_dtype == H3DIT_F32, mod + 0 * D, mod + 1 * D, h, T, D,
-                                 cfg->eps, s),
-         "rmsnorm 1");
+  if (q)  // h1 in bf16 and as MXFP8 codes for the QKV linear
+    LAUNCH(launch_rmsnorm_modulate_mx(x, cfg->x_dtype == H3DIT_F32, mod + 0 * D, mod + 1 * D, h, qa,
+                                      qas, T, D, cfg->eps, s),
+           "rmsnorm 1");
+  else
+    LAUNCH(launch_rmsnorm_modulate(x, cfg->x_dtype == H3DIT_F32, mod + 0 * D, mod + 1 * D, h, T,
+                                   D, cfg->eps, s),
+           "rmsnorm 1");
   LAUNCH(mark(3), "event record");
   {
     GemmArgs g = gemm_args(h, w->w_qkv, T, 3 * (int64_t)A, D);
@@ -256,7 +269,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.table = table;
     g.A = A;
     g.Mp = (int)p.Tp;
-    LAUNCH(linear(EPI_QKV_ROPE, g, q ? q->w_qkv : nullptr, q ? q->w_qkv_scale : nullptr),
+    LAUNCH(linear(EPI_QKV_ROPE, g, q ? q->w_qkv : nullptr, q ? q->w_qkv_scale : nullptr, qa, qas,
+                  false),
            "qkv gemm");
   }
   LAUNCH(mark(4), "event record");
@@ -268,17 +282,26 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.resid = x;
     g.gate = mod + 2 * D;
     LAUNCH(linear(cfg->x_dtype == H3DIT_F32 ? EPI_RESID_F32 : EPI_RESID_BF16, g,
-                  q ? q->w_o : nullptr, q ? q->w_o_scale : nullptr),
+                  q ? q->w_o : nullptr, q ? q->w_o_scale : nullptr, qa, qas, true),
            "output projection");
   }
   LAUNCH(mark(6), "event record");
-  LAUNCH(launch_rmsnorm_modulate(x1, true, mod + 3 * D, mod + 4 * D, h, T, D, cfg->eps, s),
-         "rmsnorm 2");
+  if (q)
+    LAUNCH(launch_rmsnorm_modulate_mx(x1, true, mod + 3 * D, mod + 4 * D, h, qa, qas, T, D,
+                                      cfg->eps, s),
+           "rmsnorm 2");
+  else
+    LAUNCH(launch_rmsnorm_modulate(x1, true, mod + 3 * D, mod + 4 * D, h, T, D, cfg->eps, s),
+           "rmsnorm 2");
   LAUNCH(mark(7), "event record");
   {
     GemmArgs g = gemm_args(h, w->w_up, T, F, D);
     g.out = u;
-    LAUNCH(linear(EPI_GELU, g, q ? q->w_up : nullptr, q ? q->w_up_scale : nullptr), "mlp up");
+    g.out_codes = qb;  // MXFP8: u also as codes for the down linear
+    g.out_scales = qbs;
+    LAUNCH(linear(q ? EPI_GELU_MX : EPI_GELU, g, q ? q->w_up : nullptr,
+                  q ? q->w_up_scale : nullptr, qa, qas, false),
+           "mlp up");
   }
   LAUNCH(mark(8), "event record");
   {
@@ -286,7 +309,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.out = out;
     g.resid = x1;
     g.gate = mod + 5 * D;
-    LAUNCH(linear(EPI_RESID_F32, g, q ? q->w_down : nullptr, q ? q->w_down_scale : nullptr),
+    LAUNCH(linear(EPI_RESID_F32, g, q ? q->w_down : nullptr, q ? q->w_down_scale : nullptr, qb,
+                  qbs, false),
            "mlp down");
   }
   LAUNCH(mark(9), "event record");
@@ -509,6 +533,10 @@ int h3dit_workspace_layout(const h3dit_config *cfg, int32_t linears, h3dit_works
   map->o = p.o;
   map->x1 = p.x1;
   map->u = p.u;
+  map->q_h2 = p.qa;
+  map->q_h2_scale = p.qas;
+  map->q_u = p.qb;
+  map->q_u_scale = p.qbs;
   return ok();
 }
 

@@ -21,6 +21,11 @@ hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *s
                                    const double *scale, void *h, int T, int D, float eps,
                                    hipStream_t s);
 
+// same, and the bf16 output also as MXFP8 codes [T, D] + scales (D % 128 == 0)
+hipError_t launch_rmsnorm_modulate_mx(const void *x, bool x_is_f32, const double *shift,
+                                      const double *scale, void *h, uint8_t *codes,
+                                      uint8_t *scales, int T, int D, float eps, hipStream_t s);
+
 // same, fp32 output (the final layer of the DiT stack)
 hipError_t launch_rmsnorm_modulate_f32out(const void *x, bool x_is_f32, const double *shift,
                                           const double *scale, float *h, int T, int D, float eps,
@@ -29,7 +34,14 @@ hipError_t launch_rmsnorm_modulate_f32out(const void *x, bool x_is_f32, const do
 // table[T, 64] float2 (cos, sin)
 hipError_t launch_rope_table(const int32_t *pos, float *table, int T, float base, hipStream_t s);
 
-enum GemmEpilogue { EPI_QKV_ROPE = 0, EPI_RESID_BF16 = 1, EPI_RESID_F32 = 2, EPI_GELU = 3, EPI_F32 = 4 };
+enum GemmEpilogue {
+  EPI_QKV_ROPE = 0,
+  EPI_RESID_BF16 = 1,
+  EPI_RESID_F32 = 2,
+  EPI_GELU = 3,
+  EPI_F32 = 4,
+  EPI_GELU_MX = 5  // EPI_GELU, and u also as MXFP8 codes + scales (MXFP8 GEMM only)
+};
 
 struct GemmArgs {
   const void *x;      // B operand rows: activations [M, K] bf16 (MXFP8: E4M3 codes)
@@ -45,6 +57,8 @@ struct GemmArgs {
   const float *table; // QKV: rope table [M, 64] float2
   int A;              // QKV: attention width
   int Mp;             // QKV: padded token count of vt
+  uint8_t *out_codes;   // GELU_MX: u as E4M3 codes [M, N]
+  uint8_t *out_scales;  // GELU_MX: u's scales (1 KB block layout, K = N)
   // Optional scratch for splitting the last, partial wave of tiles along K
   // (nullptr: never split). Set by the caller; split and full_tiles are
   // filled in by launch_gemm.

@@ -10,9 +10,6 @@
 // magnitudes of 448 and above saturating to 448 and the sign kept when the
 // value rounds to zero.
 //
-// The conversion is integer arithmetic on the bf16 bits (subnormal inputs
-// included), so it does not depend on the floating-point denormal mode.
-//
 // Layouts: codes [rows, K] bytes, row-major. Scales in 1 KB blocks, one per
 // (panel of 256 rows, K tile of 128); block (panel p, K tile t) starts at
 // byte (p * K / 128 + t) * 1024, and the scale of panel row 16 b + r
@@ -21,43 +18,11 @@
 // read them (gemm_mx.hip). Rows of the last panel past `rows` get byte 0.
 #include "common.h"
 #include "kernels.h"
+#include "mxfp8_device.h"
 
 namespace h3dit {
 
 namespace {
-
-// E4M3 code of the bf16 value with bits `v` scaled by 2^-X, X = sbyte - 127.
-__device__ __forceinline__ uint32_t e4m3_code(uint32_t v, int sbyte) {
-  const uint32_t sign = (v >> 15) & 1u;
-  const int E = (int)((v >> 7) & 0xFFu);
-  const uint32_t m = v & 0x7Fu;
-  // |v| = M * 2^e with an integer significand M < 256
-  const uint32_t M = E ? (m | 0x80u) : m;
-  const int e = E ? E - 134 : -133;
-  const int f = e - (sbyte - 127);  // |v| * 2^-X = M * 2^f
-  uint32_t code = 0;
-  if (M) {
-    const int b = 31 - __builtin_clz(M);  // M in [2^b, 2^(b+1))
-    const int p = b + f;                  // value in [2^p, 2^(p+1))
-    const int q = (p > -6 ? p : -6) - 3;  // exponent of the code spacing (subnormals: 2^-9)
-    const int sh = q - f;                 // n = round(M * 2^-sh), the value in spacings
-    uint32_t n;
-    if (sh <= 0) {
-      n = M << (-sh);
-    } else {
-      const int s = sh < 30 ? sh : 30;
-      const uint32_t half = 1u << (s - 1);
-      const uint32_t rem = M & ((1u << s) - 1u);
-      n = M >> s;
-      n += (rem > half || (rem == half && (n & 1u))) ? 1u : 0u;
-    }
-    // normal binade p: code (p + 7) * 8 + (n - 8), n in [8, 16] (16 carries into
-    // the next binade); below 2^-6 the code is n itself
-    const int c = p >= -6 ? (p + 7) * 8 + (int)n - 8 : (int)n;
-    code = (uint32_t)(c < 126 ? c : 126);  // 126 = 448, the saturation value
-  }
-  return code | (sign << 7);
-}
 
 // One workgroup per (panel of 256 rows, K tile of 128). Each pass of a wave
 // covers 4 rows of 256 bytes (16 lanes per row, 8 elements per lane); the 4
@@ -90,14 +55,12 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const bf16 *__restr
     for (int i = 0; i < 8; ++i) amax = max(amax, h[i] & 0x7FFFu);
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-    // X + 127 = floor(log2 amax) - 8 + 127 = (exponent field) - 8, at least 0
-    const int ex = (int)(amax >> 7);
-    const int sbyte = ex > 8 ? ex - 8 : 0;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= e4m3_code(h[i], sbyte) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= e4m3_code(h[4 + i], sbyte) << (8 * i);
+    const int sbyte = mx_scale_byte(amax);
+    const float inv = mx_inv_scale(sbyte);
+    const uint32_t lo = mx_code4(mx_bf16_value(h[0]), mx_bf16_value(h[1]), mx_bf16_value(h[2]),
+                                 mx_bf16_value(h[3]), inv);
+    const uint32_t hi = mx_code4(mx_bf16_value(h[4]), mx_bf16_value(h[5]), mx_bf16_value(h[6]),
+                                 mx_bf16_value(h[7]), inv);
     if (live) *reinterpret_cast<u32x2 *>(codes + (int64_t)row * K + k0) = u32x2{lo, hi};
     if ((lane & 3) == 0) sc[(kb * 16 + (rl & 15)) * 16 + (rl >> 4)] = (uint8_t)(live ? sbyte : 0);
   }

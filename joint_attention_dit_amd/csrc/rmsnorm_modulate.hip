@@ -6,8 +6,12 @@
 // DiT stack, fp32. For rows of up to 8192 elements the row stays in registers between the
 // passes, so x is read from memory once (with thousands of rows in flight the
 // L2 does not keep a row until its second pass); longer rows are read twice.
+// For the MXFP8 linears the register-row kernel can also quantise its bf16
+// output to E4M3 codes and E8M0 scales (one per 32 consecutive elements; the
+// four lanes that hold a block of 32 find its maximum with two exchanges).
 #include "common.h"
 #include "kernels.h"
+#include "mxfp8_device.h"
 
 #include <type_traits>
 
@@ -70,12 +74,13 @@ __device__ __forceinline__ void store8<float>(float *p, const double v[8]) {
 }
 
 // Row in registers: lane l holds 16-byte chunks l, l + 64, ... (at most NC).
-template <typename XT, int NC, typename OT>
-__global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(const XT *__restrict__ x,
-                                                                   const double *__restrict__ shift,
-                                                                   const double *__restrict__ scale,
-                                                                   OT *__restrict__ h, int T,
-                                                                   int D, double eps) {
+// With MX (bf16 output only), the row is also written as MXFP8 codes [T, D]
+// and scales (1 KB block layout of mxfp8_device.h).
+template <typename XT, int NC, typename OT, bool MX = false>
+__global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(
+    const XT *__restrict__ x, const double *__restrict__ shift, const double *__restrict__ scale,
+    OT *__restrict__ h, int T, int D, double eps, uint8_t *__restrict__ codes = nullptr,
+    uint8_t *__restrict__ scales = nullptr) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= T) return;
@@ -115,6 +120,25 @@ __global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(const XT *__r
         o[j] = (double)Chunk8<XT>::at(v[i], j) * r * (1.0 + scale[col]) + shift[col];
       }
       store8<OT>(hr + c * 8, o);
+      if constexpr (MX) {
+        // chunks 4m .. 4m + 3 (lanes 4m' .. 4m' + 3; D % 128 == 0, so a group of
+        // four lanes is active or idle together) form one block of 32
+        float g[8];
+        uint32_t amax = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bf16 b = to_bf16(o[j]);
+          g[j] = (float)b;
+          amax = max(amax, (uint32_t)__builtin_bit_cast(uint16_t, b) & 0x7FFFu);
+        }
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+        const int sbyte = mx_scale_byte(amax);
+        const float inv = mx_inv_scale(sbyte);
+        const u32x2 q = {mx_code4(g[0], g[1], g[2], g[3], inv), mx_code4(g[4], g[5], g[6], g[7], inv)};
+        *reinterpret_cast<u32x2 *>(codes + (int64_t)row * D + c * 8) = q;
+        if ((lane & 3) == 0) scales[mx_scale_offset(row, c >> 2, D)] = (uint8_t)sbyte;
+      }
     }
   }
 }
@@ -190,6 +214,36 @@ hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *s
                                    const double *scale, void *h, int T, int D, float eps,
                                    hipStream_t s) {
   return launch_rn(x, x_is_f32, shift, scale, static_cast<bf16 *>(h), T, D, eps, s);
+}
+
+hipError_t launch_rmsnorm_modulate_mx(const void *x, bool x_is_f32, const double *shift,
+                                      const double *scale, void *h, uint8_t *codes,
+                                      uint8_t *scales, int T, int D, float eps, hipStream_t s) {
+  const int per_lane = (int)ceil_div(D, 64 * 8);
+  if (D % 128 != 0) return hipErrorInvalidValue;
+  if (per_lane > 16) {  // long rows: the two-pass normalisation, then the quantisation
+    hipError_t e = launch_rmsnorm_modulate(x, x_is_f32, shift, scale, h, T, D, eps, s);
+    if (e != hipSuccess) return e;
+    return launch_mxfp8_quantize(h, T, D, codes, scales, s);
+  }
+  const int blocks = (int)ceil_div(T, 4);
+  auto reg = [&](auto nc_c) {
+    constexpr int NC = decltype(nc_c)::value;
+    if (x_is_f32)
+      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<float, NC, bf16, true>), dim3(blocks),
+                         dim3(256), 0, s, static_cast<const float *>(x), shift, scale,
+                         static_cast<bf16 *>(h), T, D, (double)eps, codes, scales);
+    else
+      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<bf16, NC, bf16, true>), dim3(blocks),
+                         dim3(256), 0, s, static_cast<const bf16 *>(x), shift, scale,
+                         static_cast<bf16 *>(h), T, D, (double)eps, codes, scales);
+    return hipGetLastError();
+  };
+  if (per_lane <= 1) return reg(std::integral_constant<int, 1>());
+  if (per_lane <= 4) return reg(std::integral_constant<int, 4>());
+  if (per_lane <= 8) return reg(std::integral_constant<int, 8>());
+  if (per_lane <= 11) return reg(std::integral_constant<int, 11>());
+  return reg(std::integral_constant<int, 16>());
 }
 
 hipError_t launch_rmsnorm_modulate_f32out(const void *x, bool x_is_f32, const double *shift,

@@ -269,6 +269,14 @@ def test_block_mxfp8_full_width_stages(name):
     assert np.max(np.abs(h2 - h2_ref) / (2.0 ** -8 * np.abs(h2_ref) + 1e-30)) <= 1.0
     u = f64(iv["u"])[rows]
     _check_linear(u, None, None, deq(h2), deq(w["w_up"]), "u (MLP up + GELU)", post=O.gelu_tanh)
+    # the normalisation and the GELU epilogue also write their output as MXFP8
+    # codes: bit-exact against the oracle's quantisation of the same bf16 values
+    for nm, bf, K in (("h2", h2, D), ("u", u, F)):
+        rc, rs = MX.quantize(bf)
+        gc = iv["q_" + nm].numpy()[rows]
+        gs = unpack_scales(iv["q_" + nm + "_scale"].numpy(), T, K)[rows]
+        say(f"  {nm} codes: {int(np.sum(gc != rc))} differ, scales: {int(np.sum(gs != rs))} differ")
+        assert np.array_equal(gc, rc) and np.array_equal(gs, rs), nm
     _check_linear(out[rows], x1, mv["gate2"], deq(u), deq(w["w_down"]), "out (MLP down)")
 
 
