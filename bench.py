@@ -247,12 +247,14 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cfg) -> str:
     return "\n".join(lines) + "\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n"
 
 
-def measure_stack(scfg, images: int, warmup: int, mod_table: bool = True):
+def measure_stack(scfg, images: int, warmup: int, mod_table: bool = True, linears: str = "bf16"):
     """Seconds per image of DiT compute: `scfg.steps` evaluations of the whole
     stack (patch embedding, n_blocks blocks, final layer) with an Euler update
     after each, on seeded random-init weights resident in HBM. With mod_table,
     every block's and the final layer's modulation for all steps is computed
-    first in one pass over each AdaLN weight (inside the timed region)."""
+    first in one pass over each AdaLN weight (inside the timed region). With
+    linears="mxfp8" the blocks' linear weights are quantised once before the
+    timed region (as an online MXFP8 load would) and every block runs MXFP8."""
     import torch
     from joint_attention_dit_amd import binding as B
     from joint_attention_dit_amd.inputs import make_stack_inputs
@@ -261,7 +263,18 @@ def measure_stack(scfg, images: int, warmup: int, mod_table: bool = True):
     cfg = B.config_from(scfg.block)
     gh, gw = scfg.grid
     st = B.StackConfig(scfg.n_blocks, scfg.channels, scfg.patch, gh, gw, scfg.block.text_tokens)
-    ws = torch.empty(B.h3dit_stack_workspace_size(cfg, st), dtype=torch.uint8, device="cuda")
+    mx = linears == "mxfp8"
+    qblocks = None
+    if mx:
+        qblocks = B.quantize_blocks(inp["blocks"])
+        for b in inp["blocks"]:  # only w_ada stays in use
+            for k in B.MX_LINEARS:
+                b[k] = None
+        torch.cuda.empty_cache()
+        nbytes = B.h3dit_stack_workspace_size_mxfp8(cfg, st)
+    else:
+        nbytes = B.h3dit_stack_workspace_size(cfg, st)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     latent0 = inp["latent"].clone()
     latent = latent0.clone()
     v = torch.empty_like(latent)
@@ -277,7 +290,15 @@ def measure_stack(scfg, images: int, warmup: int, mod_table: bool = True):
             B.h3dit_dit_modulation_table(cfg, st, inp["w_ada_final"], inp["blocks"], conds, table,
                                          stream)
         for k, cond in enumerate(inp["conds"]):
-            if mod_table:
+            if mx and mod_table:
+                B.h3dit_dit_forward_mod_mxfp8(cfg, st, inp["w_patch"], inp["w_final"],
+                                              inp["blocks"], qblocks, latent, inp["text"],
+                                              table[k], inp["positions"], v, ws, stream)
+            elif mx:
+                B.h3dit_dit_forward_mxfp8(cfg, st, inp["w_patch"], inp["w_ada_final"],
+                                          inp["w_final"], inp["blocks"], qblocks, latent,
+                                          inp["text"], cond, inp["positions"], v, ws, stream)
+            elif mod_table:
                 B.h3dit_dit_forward_mod(cfg, st, inp["w_patch"], inp["w_final"], inp["blocks"],
                                         latent, inp["text"], table[k], inp["positions"], v, ws,
                                         stream)
@@ -464,7 +485,7 @@ def main():
         from joint_attention_dit_amd.inputs import STACK_CONFIGS
         scfg = STACK_CONFIGS["dit_2048"]
         sec, ok = measure_stack(scfg, images=max(args.steps // 10, 1), warmup=1 if args.warmup else 0,
-                                mod_table=not args.no_mod_table)
+                                mod_table=not args.no_mod_table, linears=args.linears)
         fl = stack_flops(scfg)
         print(json.dumps({
             "metric": "DiT compute images/s (50 blocks x 6 denoising steps, 2048x2048)",
@@ -472,7 +493,9 @@ def main():
             "value": round(1.0 / sec, 4), "unit": "images/s", "n_gpus": 1,
             "ms_per_image": round(sec * 1e3, 2),
             "ms_per_block": round(sec * 1e3 / (scfg.n_blocks * scfg.steps), 4),
-            "higher_is_better": True, "dtype": "bf16", "data": "synthetic (seeded, drawn on the GPU)",
+            "higher_is_better": True,
+            "dtype": "bf16" if args.linears == "bf16" else "mxfp8 linears (e4m3 + e8m0/32), bf16 attention",
+            "data": "synthetic (seeded, drawn on the GPU)",
             "config": {"workload": scfg.description, "n_blocks": scfg.n_blocks, "steps": scfg.steps,
                        "n_tokens": scfg.block.n_tokens, "latent": list(scfg.latent_shape)},
             "tflops": round(fl / sec / 1e12, 1),

@@ -343,6 +343,26 @@ int h3dit_dit_forward_mod(const h3dit_config *cfg, const h3dit_stack_config *st,
                           const double *mods, const int32_t *positions, float *v, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* The DiT evaluation with every block's four linears in MXFP8 (vLLM blog "H3-Image
+ * Day-0 Support", section Inference Optimizations: MXFP8 GEMMs for the DiT's
+ * linears). q holds st->n_blocks entries, block l's weights quantised with
+ * h3dit_mxfp8_quantize; w->blocks[l] then supplies only w_ada (and is not read
+ * at all by the _mod form). hidden and ffn must be multiples of 128. The patch
+ * embedding and final projection stay fp32. Workspace from
+ * h3dit_stack_workspace_size_mxfp8 (host-only). q may be NULL when n_blocks is 0. */
+int h3dit_stack_workspace_size_mxfp8(const h3dit_config *cfg, const h3dit_stack_config *st,
+                                     size_t *bytes);
+int h3dit_dit_forward_mxfp8(const h3dit_config *cfg, const h3dit_stack_config *st,
+                            const h3dit_stack_weights *w, const h3dit_mxfp8_weights *q,
+                            const float *latent, const float *text, const float *cond,
+                            const int32_t *positions, float *v, void *workspace,
+                            size_t workspace_bytes, void *stream);
+int h3dit_dit_forward_mod_mxfp8(const h3dit_config *cfg, const h3dit_stack_config *st,
+                                const h3dit_stack_weights *w, const h3dit_mxfp8_weights *q,
+                                const float *latent, const float *text, const double *mods,
+                                const int32_t *positions, float *v, void *workspace,
+                                size_t workspace_bytes, void *stream);
+
 /* latent[i] += dt * v[i] for i < n (fp32): the explicit Euler update between
  * denoising steps. */
 int h3dit_latent_step(float *latent, const float *v, float dt, int64_t n, void *stream);

@@ -30,7 +30,8 @@ EXPORTED = (
     "h3dit_last_error", "h3dit_modulation_table", "h3dit_dit_modulation_table",
     "h3dit_dit_forward_mod", "h3dit_mxfp8_scale_bytes", "h3dit_mxfp8_quantize",
     "h3dit_linear_mxfp8", "h3dit_workspace_size_mxfp8", "h3dit_block_forward_mxfp8",
-    "h3dit_block_forward_mxfp8_timed", "h3dit_workspace_layout",
+    "h3dit_block_forward_mxfp8_timed", "h3dit_workspace_layout", "h3dit_stack_workspace_size_mxfp8",
+    "h3dit_dit_forward_mxfp8", "h3dit_dit_forward_mod_mxfp8",
 )
 
 
@@ -116,6 +117,12 @@ def load_library() -> ctypes.CDLL:
         "h3dit_linear_mxfp8": [vp, vp, vp, vp, i32, i32, i32, vp, vp],
         "h3dit_workspace_size_mxfp8": [cfgp, ctypes.POINTER(sz)],
         "h3dit_workspace_layout": [cfgp, i32, ctypes.POINTER(WorkspaceMap)],
+        "h3dit_stack_workspace_size_mxfp8": [cfgp, ctypes.POINTER(StackConfig), ctypes.POINTER(sz)],
+        "h3dit_dit_forward_mxfp8": [cfgp, ctypes.POINTER(StackConfig), ctypes.POINTER(StackWeights),
+                                    ctypes.POINTER(MxWeights), vp, vp, vp, vp, vp, vp, sz, vp],
+        "h3dit_dit_forward_mod_mxfp8": [cfgp, ctypes.POINTER(StackConfig),
+                                        ctypes.POINTER(StackWeights), ctypes.POINTER(MxWeights),
+                                        vp, vp, vp, vp, vp, vp, sz, vp],
         "h3dit_block_forward_mxfp8": [cfgp, vp, vp, ctypes.POINTER(Weights),
                                       ctypes.POINTER(MxWeights), vp, vp, vp, sz, vp],
         "h3dit_block_forward_mxfp8_timed": [cfgp, vp, vp, ctypes.POINTER(Weights),
@@ -321,6 +328,61 @@ def h3dit_dit_forward_mod(cfg: Config, st: StackConfig, w_patch, w_final,
         ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), _ptr(latent), _ptr(text),
         _ptr(mods), _ptr(positions), _ptr(v), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)), "h3dit_dit_forward_mod")
+
+
+def h3dit_stack_workspace_size_mxfp8(cfg: Config, st: StackConfig) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().h3dit_stack_workspace_size_mxfp8(ctypes.byref(cfg), ctypes.byref(st),
+                                                           ctypes.byref(n)),
+           "h3dit_stack_workspace_size_mxfp8")
+    return n.value
+
+
+def quantize_blocks(blocks: Sequence[Dict[str, torch.Tensor]], stream=None):
+    """MXFP8 codes + scales of every block's four linear weights (on their device)."""
+    out = []
+    for b in blocks:
+        q = {}
+        for k in MX_LINEARS:
+            q[k], q[k + "_scale"] = mxfp8_quantize(b[k], stream)
+        out.append(q)
+    return out
+
+
+def _mx_array(qblocks):
+    return (MxWeights * max(len(qblocks), 1))(*[mx_weights_struct(q) for q in qblocks])
+
+
+def h3dit_dit_forward_mxfp8(cfg: Config, st: StackConfig, w_patch, w_ada_final, w_final,
+                            blocks: Sequence[Dict[str, torch.Tensor]], qblocks, latent, text,
+                            cond, positions, v, workspace, stream=None) -> None:
+    """h3dit_dit_forward with MXFP8 linears; blocks supply w_ada, qblocks the
+    quantised linears (quantize_blocks)."""
+    sw, arr = _stack_weights(w_patch, w_ada_final, w_final, [_ada_only(b) for b in blocks])
+    qa = _mx_array(qblocks)
+    _check(load_library().h3dit_dit_forward_mxfp8(
+        ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw),
+        ctypes.cast(qa, ctypes.POINTER(MxWeights)) if qblocks else None, _ptr(latent), _ptr(text),
+        _ptr(cond), _ptr(positions), _ptr(v), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "h3dit_dit_forward_mxfp8")
+
+
+def h3dit_dit_forward_mod_mxfp8(cfg: Config, st: StackConfig, w_patch, w_final,
+                                blocks: Sequence[Dict[str, torch.Tensor]], qblocks, latent, text,
+                                mods, positions, v, workspace, stream=None) -> None:
+    sw, arr = _stack_weights(w_patch, None, w_final, [_ada_only(b) for b in blocks])
+    qa = _mx_array(qblocks)
+    _check(load_library().h3dit_dit_forward_mod_mxfp8(
+        ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw),
+        ctypes.cast(qa, ctypes.POINTER(MxWeights)) if qblocks else None, _ptr(latent), _ptr(text),
+        _ptr(mods), _ptr(positions), _ptr(v), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)),
+        "h3dit_dit_forward_mod_mxfp8")
+
+
+def _ada_only(b: Dict[str, torch.Tensor]) -> Dict[str, Optional[torch.Tensor]]:
+    """A block's weight dict for the MXFP8 stack: only w_ada is read."""
+    return {"w_ada": b.get("w_ada"), "w_qkv": None, "w_o": None, "w_up": None, "w_down": None}
 
 
 def h3dit_latent_step(latent: torch.Tensor, v: torch.Tensor, dt: float, stream=None) -> None:

@@ -345,14 +345,14 @@ h3dit_config stack_block_config(const h3dit_config *cfg) {
   return c;
 }
 
-StackPlan make_stack_plan(const h3dit_config *cfg, const h3dit_stack_config *st) {
+StackPlan make_stack_plan(const h3dit_config *cfg, const h3dit_stack_config *st, bool mx = false) {
   StackPlan p;
   p.T = cfg->n_tokens;
   p.D = cfg->hidden;
   p.Ti = (int64_t)st->grid_h * st->grid_w;
   p.F = (int64_t)st->channels * st->patch * st->patch;
   const h3dit_config bc = stack_block_config(cfg);
-  p.block_bytes = make_plan(&bc).total;
+  p.block_bytes = make_plan(&bc, mx).total;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -372,10 +372,12 @@ StackPlan make_stack_plan(const h3dit_config *cfg, const h3dit_stack_config *st)
 
 // mods: every block's modulation and the final layer's, fp64 [(n_blocks + 1) * 6D]
 // (entry n_blocks holds the final layer's shift and scale in its first 2D values),
-// or NULL to compute them from cond.
+// or NULL to compute them from cond. q: n_blocks MXFP8 weight sets (the blocks'
+// linears in MXFP8), or NULL for bf16 linears.
 int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_stack_weights *w,
              const float *latent, const float *text, const float *cond, const int32_t *positions,
-             float *v, void *ws, size_t ws_bytes, void *stream, const double *mods = nullptr) {
+             float *v, void *ws, size_t ws_bytes, void *stream, const double *mods = nullptr,
+             const h3dit_mxfp8_weights *q = nullptr) {
   {
     const int st_ = check_stack(cfg, st);
     if (st_ != H3DIT_OK) return st_;
@@ -391,7 +393,10 @@ int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_
   CHECK_PTR(positions);
   CHECK_PTR(v);
   CHECK_PTR(ws);
-  const StackPlan p = make_stack_plan(cfg, st);
+  if (q && st->n_blocks > 0 && (cfg->hidden % 128 != 0 || cfg->ffn % 128 != 0))
+    return fail(H3DIT_EUNSUPPORTED, "MXFP8 linears need hidden and ffn multiples of 128 "
+                "(got %d, %d)", cfg->hidden, cfg->ffn);
+  const StackPlan p = make_stack_plan(cfg, st, q != nullptr);
   if (ws_bytes < p.total)
     return fail(H3DIT_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, p.total);
   {
@@ -401,10 +406,22 @@ int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_
   }
   for (int l = 0; l < st->n_blocks; ++l) {  // every block's weights, before anything is enqueued
     const h3dit_weights &b = w->blocks[l];
-    if ((!mods && !b.w_ada) || !b.w_qkv || !b.w_o || !b.w_up || !b.w_down)
-      return fail(H3DIT_EINVAL, "block %d has a NULL weight pointer", l);
-    if ((!mods && !aligned16(b.w_ada)) || !aligned16(b.w_qkv) || !aligned16(b.w_o) ||
-        !aligned16(b.w_up) || !aligned16(b.w_down))
+    const void *lin[8] = {b.w_qkv, b.w_o, b.w_up, b.w_down, nullptr, nullptr, nullptr, nullptr};
+    int nlin = 4;
+    if (q) {
+      const h3dit_mxfp8_weights &m = q[l];
+      const void *mq[8] = {m.w_qkv, m.w_qkv_scale, m.w_o, m.w_o_scale,
+                           m.w_up,  m.w_up_scale,  m.w_down, m.w_down_scale};
+      for (int i = 0; i < 8; ++i) lin[i] = mq[i];
+      nlin = 8;
+    }
+    bool null = !mods && !b.w_ada, misaligned = !mods && !aligned16(b.w_ada);
+    for (int i = 0; i < nlin; ++i) {
+      null = null || !lin[i];
+      misaligned = misaligned || !aligned16(lin[i]);
+    }
+    if (null) return fail(H3DIT_EINVAL, "block %d has a NULL weight pointer", l);
+    if (misaligned)
       return fail(H3DIT_EALIGN, "block %d has a weight pointer that is not 16-byte aligned", l);
   }
 
@@ -428,7 +445,7 @@ int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_
   for (int l = 0; l < st->n_blocks; ++l) {
     const int rc = forward_impl(&bc, cur, cond, &w->blocks[l], positions, nxt, at<void>(ws, p.block),
                                 p.block_bytes, stream, nullptr, 0,
-                                mods ? mods + (size_t)l * 6 * D : nullptr);
+                                mods ? mods + (size_t)l * 6 * D : nullptr, q ? &q[l] : nullptr);
     if (rc != H3DIT_OK) return rc;
     float *t = cur;
     cur = nxt;
@@ -505,6 +522,37 @@ int h3dit_dit_forward_mod(const h3dit_config *cfg, const h3dit_stack_config *st,
   CHECK_PTR(mods);
   return dit_impl(cfg, st, w, latent, text, nullptr, positions, v, workspace, workspace_bytes,
                   stream, mods);
+}
+
+int h3dit_stack_workspace_size_mxfp8(const h3dit_config *cfg, const h3dit_stack_config *st,
+                                     size_t *bytes) {
+  const int rc = check_stack(cfg, st);
+  if (rc != H3DIT_OK) return rc;
+  if (!bytes) return fail(H3DIT_EINVAL, "bytes is NULL");
+  *bytes = make_stack_plan(cfg, st, true).total;
+  return ok();
+}
+
+int h3dit_dit_forward_mxfp8(const h3dit_config *cfg, const h3dit_stack_config *st,
+                            const h3dit_stack_weights *w, const h3dit_mxfp8_weights *q,
+                            const float *latent, const float *text, const float *cond,
+                            const int32_t *positions, float *v, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  if (!q && st && st->n_blocks > 0) return fail(H3DIT_EINVAL, "q is NULL");
+  // (with no blocks there is nothing to quantise: q may be NULL)
+  return dit_impl(cfg, st, w, latent, text, cond, positions, v, workspace, workspace_bytes, stream,
+                  nullptr, q);
+}
+
+int h3dit_dit_forward_mod_mxfp8(const h3dit_config *cfg, const h3dit_stack_config *st,
+                                const h3dit_stack_weights *w, const h3dit_mxfp8_weights *q,
+                                const float *latent, const float *text, const double *mods,
+                                const int32_t *positions, float *v, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  CHECK_PTR(mods);
+  if (!q && st && st->n_blocks > 0) return fail(H3DIT_EINVAL, "q is NULL");
+  return dit_impl(cfg, st, w, latent, text, nullptr, positions, v, workspace, workspace_bytes,
+                  stream, mods, q);
 }
 
 int h3dit_latent_step(float *latent, const float *v, float dt, int64_t n, void *stream) {

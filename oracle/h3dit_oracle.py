@@ -277,13 +277,14 @@ def final_layer(x_img: np.ndarray, cond: np.ndarray, w_ada_final: np.ndarray,
 def dit_forward(latent: np.ndarray, text: np.ndarray, cond: np.ndarray, w_patch: np.ndarray,
                 w_ada_final: np.ndarray, w_final: np.ndarray, blocks, pos: np.ndarray,
                 heads: int, patch: int, eps: float = 1e-6, rope_base: float = 10000.0,
-                mode: str = "contract") -> np.ndarray:
-    """One DiT evaluation: v [C, H, W] for latent [C, H, W] (see module notes)."""
+                mode: str = "contract", linears: str = "bf16") -> np.ndarray:
+    """One DiT evaluation: v [C, H, W] for latent [C, H, W] (see module notes).
+    linears="mxfp8": every block's four linears in MXFP8 (see block_forward)."""
     C, H, W = latent.shape
     x = np.concatenate([text, patchify(latent, patch) @ w_patch.T], axis=0)
     for w in blocks:
         x = block_forward(x, cond, w, pos, heads=heads, eps=eps, rope_base=rope_base,
-                          mode=mode)["out"]
+                          mode=mode, linears=linears)["out"]
     vt = final_layer(x[text.shape[0]:], cond, w_ada_final, w_final, eps)
     return unpatchify(vt, C, patch, H // patch, W // patch)
 

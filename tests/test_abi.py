@@ -290,3 +290,33 @@ def test_mxfp8_forward_validation(lib):
     assert _forward_mx(lib, full_cfg(), q=q) == B.H3DIT_EINVAL
     need = B.h3dit_workspace_size_mxfp8(full_cfg())
     assert _forward_mx(lib, full_cfg(), ws_bytes=need - 1) == B.H3DIT_EWORKSPACE
+
+
+def _dit_mx(lib, cfg, st, q="ok", ws_bytes=1 << 40, blocks=2):
+    p = {k: 0x100000000 * (i + 1) for i, k in enumerate(
+        ["latent", "text", "cond", "pos", "v", "ws", "wp", "wa", "wf"])}
+    arr = (B.Weights * blocks)(*[B.Weights(0x20000000000 + 0x1000000000 * b, 0, 0, 0, 0)
+                                 for b in range(blocks)])
+    sw = B.StackWeights(p["wp"], p["wa"], p["wf"], ctypes.cast(arr, ctypes.POINTER(B.Weights)))
+    qarr = (B.MxWeights * blocks)(*[B.MxWeights(*[0x40000000000 + 0x1000000000 * (8 * b + j)
+                                                  for j in range(8)]) for b in range(blocks)])
+    if q == "null_scale":
+        qarr[blocks - 1].w_up_scale = None
+    qp = None if q is None else ctypes.cast(qarr, ctypes.POINTER(B.MxWeights))
+    return lib.h3dit_dit_forward_mxfp8(ctypes.byref(cfg), ctypes.byref(st), ctypes.byref(sw), qp,
+                                       p["latent"], p["text"], p["cond"], p["pos"], p["v"],
+                                       p["ws"], ws_bytes, None)
+
+
+def test_dit_forward_mxfp8_validation(lib):
+    cfg = B.make_config(5376, 56, 14336, 4352, B.H3DIT_F32)
+    st = stack_cfg()
+    assert _dit_mx(lib, cfg, st, q=None) == B.H3DIT_EINVAL
+    assert "q is NULL" in lib.h3dit_last_error().decode()
+    assert _dit_mx(lib, cfg, st, q="null_scale") == B.H3DIT_EINVAL
+    assert "block 1" in lib.h3dit_last_error().decode()
+    assert _dit_mx(lib, B.make_config(5312, 56, 14336, 4352, B.H3DIT_F32), st) == \
+        B.H3DIT_EUNSUPPORTED
+    need = B.h3dit_stack_workspace_size_mxfp8(cfg, st)
+    assert need > B.h3dit_stack_workspace_size(cfg, st)
+    assert _dit_mx(lib, cfg, st, ws_bytes=need - 1) == B.H3DIT_EWORKSPACE
