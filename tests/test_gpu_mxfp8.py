@@ -160,6 +160,19 @@ def test_block_mxfp8_small_all_rows(cfg):
         f"max_abs/rms {e['max_abs_over_rms']:.2e}")
 
 
+@pytest.mark.parametrize("T_text,grid", [(1, ()), (65, ()), (0, ((8, 16, 0),))],
+                         ids=["T1", "T65", "T128"])
+def test_block_mxfp8_edge_token_counts(T_text, grid):
+    """Token counts below one 256-row panel, ragged against it, and exactly
+    half of it, at the block bar against the oracle's MXFP8 block."""
+    cfg = small_config("edge", hidden=256, heads=2, ffn=512, text_tokens=T_text, images=grid)
+    inp = make_inputs(cfg, seed=11)
+    say(f"[mxfp8] edge T={cfg.n_tokens}")
+    blk = B.Block(cfg, inp, linears="mxfp8")
+    got = host(blk.forward()).astype(np.float64)
+    assert_block_parity(got, mx_reference(cfg, inp)["out"], f"mxfp8 edge T={cfg.n_tokens}")
+
+
 def test_block_mxfp8_deterministic_and_weights_unchanged():
     cfg = MID
     inp = cached_case(cfg)
@@ -198,7 +211,7 @@ def _check_linear(got, resid, gate, xd, wd, what, post=None):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["2048", "4096"])
+@pytest.mark.parametrize("name", ["2048", "4096", "nonsquare"])
 def test_block_mxfp8_full_width_stages(name):
     """Full-width MXFP8 block, stage by stage on 256 seeded rows: each linear
     against the oracle's MXFP8 linear of the GPU's own bf16 input for it (its
