@@ -57,10 +57,11 @@ def test_workspace_size_plan():
     Tp = B.h3dit_padded_tokens(T)
     assert Tp == 16896 and B.h3dit_padded_tokens(288) == 320 and B.h3dit_padded_tokens(1) == 64
     lower = 6 * D * 8 + 128 * T * 4 + 2 * T * D + 4 * T * A + 2 * A * Tp + 2 * T * A + 4 * T * D + 2 * T * F
-    # plus the scratch for K slices of a GEMM's last wave: at 16896 tokens the MLP up
-    # GEMM has 56 x 66 = 3696 tiles, 112 of them in the last wave of 256 CUs, each
-    # split in two 256 x 256 fp32 slices
-    split = 112 * 2 * 256 * 256 * 4
+    # plus the scratch for K slices of a GEMM's last wave (the largest of the four):
+    # at 16896 tokens the QKV GEMM has 84 x 66 = 5544 tiles, 168 of them in the
+    # last wave of 256 CUs, each cut into three 256 x 256 fp32 slices (two waves
+    # of thirds instead of one whole wave); MLP up has 112 left, cut in two
+    split = max(168 * 3, 112 * 2) * 256 * 256 * 4
     assert lower + split <= n <= lower + split + 9 * 256
     assert B.h3dit_workspace_size(B.make_config(256, 2, 1024, 1)) > 0
 
