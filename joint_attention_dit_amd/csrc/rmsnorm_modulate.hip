@@ -73,71 +73,90 @@ __device__ __forceinline__ void store8<float>(float *p, const double v[8]) {
   *reinterpret_cast<f32x4 *>(p + 4) = b;
 }
 
-// Row in registers: lane l holds 16-byte chunks l, l + 64, ... (at most NC).
-// With MX (bf16 output only), the row is also written as MXFP8 codes [T, D]
+// Rows in registers: each wave normalises R rows; lane l holds their 16-byte
+// chunks l, l + 64, ... (at most NC), and reads the fp64 shift and scale of its
+// columns once for all R rows (for bf16 rows they are 8x the row's own bytes).
+// R = 2 for bf16 rows; fp32 rows take twice the registers, and two of them
+// would leave one wave per SIMD, so they go one per wave.
+// With MX (bf16 output only), the rows are also written as MXFP8 codes [T, D]
 // and scales (1 KB block layout of mxfp8_device.h).
-template <typename XT, int NC, typename OT, bool MX = false>
+template <typename XT, int NC, typename OT, bool MX = false, int R = (sizeof(XT) == 2 ? 2 : 1)>
 __global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(
     const XT *__restrict__ x, const double *__restrict__ shift, const double *__restrict__ scale,
     OT *__restrict__ h, int T, int D, double eps, uint8_t *__restrict__ codes = nullptr,
     uint8_t *__restrict__ scales = nullptr) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= T) return;
-  const XT *xr = x + (int64_t)row * D;
-  OT *hr = h + (int64_t)row * D;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
+  if (row0 >= T) return;
   const int chunks = D >> 3;
 
-  typename Chunk8<XT>::raw v[NC];
+  typename Chunk8<XT>::raw v[R][NC];
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int c = lane + 64 * i;
-    if (c < chunks) v[i] = Chunk8<XT>::fetch(xr + c * 8);
-  }
-  double ss = 0.0;
+  for (int k = 0; k < R; ++k) {
+    const XT *xr = x + (int64_t)min(row0 + k, T - 1) * D;
 #pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    if (lane + 64 * i < chunks) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double e = (double)Chunk8<XT>::at(v[i], j);
-        ss += e * e;
-      }
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) v[k][i] = Chunk8<XT>::fetch(xr + c * 8);
     }
   }
+  double rs[R];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  const double r = 1.0 / sqrt(ss / (double)D + eps);
+  for (int k = 0; k < R; ++k) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if (lane + 64 * i < chunks) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double e = (double)Chunk8<XT>::at(v[k][i], j);
+          ss += e * e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    rs[k] = 1.0 / sqrt(ss / (double)D + eps);
+  }
 
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     const int c = lane + 64 * i;
     if (c < chunks) {
-      double o[8];
+      double sc1[8], sh[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int col = c * 8 + j;
-        o[j] = (double)Chunk8<XT>::at(v[i], j) * r * (1.0 + scale[col]) + shift[col];
+        sc1[j] = 1.0 + scale[c * 8 + j];
+        sh[j] = shift[c * 8 + j];
       }
-      store8<OT>(hr + c * 8, o);
-      if constexpr (MX) {
-        // chunks 4m .. 4m + 3 (lanes 4m' .. 4m' + 3; D % 128 == 0, so a group of
-        // four lanes is active or idle together) form one block of 32
-        float g[8];
-        uint32_t amax = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bf16 b = to_bf16(o[j]);
-          g[j] = (float)b;
-          amax = max(amax, (uint32_t)__builtin_bit_cast(uint16_t, b) & 0x7FFFu);
+      for (int k = 0; k < R; ++k) {
+        const int row = row0 + k;
+        if (row >= T) break;  // uniform across the wave
+        double o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = (double)Chunk8<XT>::at(v[k][i], j) * rs[k] * sc1[j] + sh[j];
+        store8<OT>(h + (int64_t)row * D + c * 8, o);
+        if constexpr (MX) {
+          // chunks 4m .. 4m + 3 (lanes 4m' .. 4m' + 3; D % 128 == 0, so a group
+          // of four lanes is active or idle together) form one block of 32
+          float g[8];
+          uint32_t amax = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const bf16 b = to_bf16(o[j]);
+            g[j] = (float)b;
+            amax = max(amax, (uint32_t)__builtin_bit_cast(uint16_t, b) & 0x7FFFu);
+          }
+          amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+          amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+          const int sbyte = mx_scale_byte(amax);
+          const float inv = mx_inv_scale(sbyte);
+          const u32x2 q = {mx_code4(g[0], g[1], g[2], g[3], inv),
+                           mx_code4(g[4], g[5], g[6], g[7], inv)};
+          *reinterpret_cast<u32x2 *>(codes + (int64_t)row * D + c * 8) = q;
+          if ((lane & 3) == 0) scales[mx_scale_offset(row, c >> 2, D)] = (uint8_t)sbyte;
         }
-        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-        const int sbyte = mx_scale_byte(amax);
-        const float inv = mx_inv_scale(sbyte);
-        const u32x2 q = {mx_code4(g[0], g[1], g[2], g[3], inv), mx_code4(g[4], g[5], g[6], g[7], inv)};
-        *reinterpret_cast<u32x2 *>(codes + (int64_t)row * D + c * 8) = q;
-        if ((lane & 3) == 0) scales[mx_scale_offset(row, c >> 2, D)] = (uint8_t)sbyte;
       }
     }
   }
@@ -185,14 +204,15 @@ template <typename OT>
 static hipError_t launch_rn(const void *x, bool x_is_f32, const double *shift, const double *scale,
                             OT *h, int T, int D, float eps, hipStream_t s) {
   const int blocks = (int)ceil_div(T, 4);
+  const int reg_blocks = (int)ceil_div(T, x_is_f32 ? 4 : 8);  // 4 waves of 1 (fp32) or 2 rows
   auto reg = [&](auto nc_c) {
     constexpr int NC = decltype(nc_c)::value;
     if (x_is_f32)
-      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<float, NC, OT>), dim3(blocks), dim3(256), 0,
-                         s, static_cast<const float *>(x), shift, scale, h, T, D, (double)eps);
+      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<float, NC, OT>), dim3(reg_blocks), dim3(256),
+                         0, s, static_cast<const float *>(x), shift, scale, h, T, D, (double)eps);
     else
-      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<bf16, NC, OT>), dim3(blocks), dim3(256), 0,
-                         s, static_cast<const bf16 *>(x), shift, scale, h, T, D, (double)eps);
+      hipLaunchKernelGGL((rmsnorm_modulate_reg_kernel<bf16, NC, OT>), dim3(reg_blocks), dim3(256),
+                         0, s, static_cast<const bf16 *>(x), shift, scale, h, T, D, (double)eps);
     return hipGetLastError();
   };
   const int per_lane = (int)ceil_div(D, 64 * 8);  // 16-byte chunks per lane
@@ -226,7 +246,7 @@ hipError_t launch_rmsnorm_modulate_mx(const void *x, bool x_is_f32, const double
     if (e != hipSuccess) return e;
     return launch_mxfp8_quantize(h, T, D, codes, scales, s);
   }
-  const int blocks = (int)ceil_div(T, 4);
+  const int blocks = (int)ceil_div(T, x_is_f32 ? 4 : 8);  // 4 waves of 1 (fp32) or 2 rows
   auto reg = [&](auto nc_c) {
     constexpr int NC = decltype(nc_c)::value;
     if (x_is_f32)
