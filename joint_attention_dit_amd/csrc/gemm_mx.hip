@@ -15,15 +15,23 @@
 // Tiling: 256 features x 256 tokens per workgroup, eight waves of 128 x 64,
 // one K tile of 128 per LDS stage: a tile row is one 128-byte segment (the
 // same copy shape as the bf16 kernel's 64-wide bf16 tiles) and one scaled
-// product per 16 x 16 block. Operand tiles have two stages each (4 x 32 KB)
-// and the scale tiles (1 KB per operand and K tile, one contiguous copy) two
-// stages each after them. Per K tile a wave issues its 32 products column
-// block by column block; the barrier sits after the first column block, when
-// every wave has its fragments of the current tile in registers (the stages
-// take tile kt + 2) and the next tile has landed. Fragments of the next tile
-// are read in place: a token fragment once its 8 products have issued, a
-// feature fragment once its last product has. LDS rows use the bf16 kernel's
-// swizzle (16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7)).
+// product per 16 x 16 block. Operand tiles have two stages each (4 x 32 KB),
+// followed by two 1 KB scale stages per operand (each wave copies 1/8 of a
+// scale tile with 8 lanes enabled inside the copy's own asm block).
+//
+// Per K tile a wave runs its 8 feature blocks against its 4 token blocks,
+// feature block by feature block. The fragments are twice as wide as bf16 ones
+// (8 VGPRs), so the feature fragments live in a ring of 4 slots (block i in
+// slot i mod 4): once block i's four products have issued, its slot is
+// refilled with block i + 4 of the same tile or, from block 4 on, with block
+// i - 4 of the next tile; the token fragments are re-read in place during the
+// last feature block. The barrier sits after feature block 4, when every wave
+// has read all its fragments of the current tile (its stages then take tile
+// kt + 2) and every copy of tile kt + 1 has landed. The K-tile body has no
+// branch (a conditional copy splits it into basic blocks, across which LLVM
+// moves the side-effect-free products past the scheduling barriers and spills):
+// past the end, the last tile is copied again into the free stage. LDS rows use
+// the bf16 kernel's swizzle (16-byte chunk c of row r at chunk c ^ ((r >> 1) & 7)).
 #include "gemm_common.h"
 
 #include <type_traits>
