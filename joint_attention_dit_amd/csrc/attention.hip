@@ -74,10 +74,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 5, c = lane & 31;
-  const int h = blockIdx.y;
+  // Work order: the dispatcher hands workgroup i to XCD i % 8. The linear id
+  // is remapped so that each XCD receives a contiguous range of (head, query
+  // tile) items, head-major: the workgroups in flight on one XCD then work on
+  // the same one or two heads and stream the same K and V tiles through its L2.
+  const int qtiles = (int)ceil_div(T, QT);
+  int h, qt;
+  {
+    const int n = (int)gridDim.x, bid = (int)blockIdx.x;
+    const int xcd = bid & 7, idx = bid >> 3, q = n >> 3, r = n & 7;
+    const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+    h = L / qtiles;
+    qt = L - h * qtiles;
+  }
   const int A = H * 128;
   const int ldqk = 2 * A;
-  const int q0 = blockIdx.x * QT + wave * 32;
+  const int q0 = qt * QT + wave * 32;
   const int ntiles = (int)ceil_div(T, KT);
 
   // this lane's query fragments: Q[q0 + c][16 s + 8 G .. +7], s = 0..7
@@ -322,7 +334,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
 
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
                             hipStream_t s) {
-  dim3 grid((unsigned)ceil_div(T, QT), (unsigned)H);
+  dim3 grid((unsigned)(ceil_div(T, QT) * H));
   hipLaunchKernelGGL(attention_kernel, grid, dim3(NTHREADS), 0, s, static_cast<const bf16 *>(qk),
                      static_cast<const bf16 *>(vt), static_cast<bf16 *>(o), T, H, Tp);
   return hipGetLastError();
