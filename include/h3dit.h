@@ -117,8 +117,8 @@ int h3dit_block_forward_timed(const h3dit_config *cfg, const void *x, const floa
  * (linears = 0) or h3dit_block_forward_mxfp8 (linears = 1) has completed, the
  * workspace holds: mod (fp64 [6D]), table (fp32 [T, 64, 2] RoPE cos/sin), h
  * (bf16 [T, D], the second normalisation's h2), qk (bf16 [T, 2A], q rotated
- * and scaled, then k rotated), vt (bf16 [H, 128, Tp], V transposed, token t at
- * column t with bits 2 and 3 exchanged, zero past T), o (bf16 [T, A]), x1
+ * and scaled, then k rotated), vt (bf16 [H, 128, Tp], V transposed, token t in
+ * the column described at h3dit_qkv_rope, zero past T), o (bf16 [T, A]), x1
  * (fp32 [T, D]) and u (bf16 [T, F]). For inspection and tests; the contents
  * are only defined between forwards on the same workspace. */
 typedef struct {
@@ -167,9 +167,11 @@ int h3dit_rope_table(const h3dit_config *cfg, const int32_t *positions, float *t
  *      columns A..2A-1 = bf16(rope(k)); q and k are the fp32 products, rounded
  *      once after the rotation.
  *   vt [H, 128, Tp] bf16 with Tp = h3dit_padded_tokens(T): v transposed per head;
- *      the value of token t sits in column t with bits 2 and 3 of t exchanged
- *      (the order in which the attention kernel's matrix-core fragments take
- *      keys); columns of tokens T..Tp-1 are written as zero. */
+ *      the value of token t sits in column c(t) = (t & ~28) | ((t & 12) << 1)
+ *      | ((t & 16) >> 2), i.e. bits 4, 3, 2 of t moved to bits 2, 4, 3 within
+ *      each group of 32 tokens (the order in which the attention kernel's
+ *      matrix-core fragments take keys); columns of tokens T..Tp-1 are written
+ *      as zero. */
 int h3dit_qkv_rope(const h3dit_config *cfg, const void *h, const void *w_qkv, const float *table,
                    void *qk, void *vt, void *stream);
 

@@ -6,33 +6,43 @@
 //
 // Work split: a workgroup owns 256 queries of one head (eight waves of 32, two
 // waves per SIMD). Each wave computes the transposed score tile S^T = K Q^T
-// with the 32x32x16 bf16 MFMA, so a lane holds 32 of the 64 scores of ONE
-// query (the other 32 sit in lane l ^ 32). The output is accumulated
-// transposed as well, O^T += V^T P^T; the MFMA's K slots of that product are
-// assigned to keys in the order in which the score registers hold them (lane
-// half G holds keys 4G..4G+3 and 8+4G..8+4G+3 of every 16), and V^T is stored
-// in global memory with bits 2 and 3 of the key index exchanged, so each such
-// fragment is one 16-byte read.
+// with the 16x16x32 bf16 MFMA: on random operands the chip runs into its power
+// limit, and this product moves half the accumulator data per flop of the
+// 32x32x16 one. Lane l = 16 g + r holds, for each of its two queries (r and
+// 16 + r of the wave), the scores of keys 16 b + 4 g .. +3 of every 16-key
+// block b: 16 of the tile's 64 keys; the other 48 sit in lanes l ^ 16, l ^ 32,
+// l ^ 48. The output is accumulated transposed as well, O^T += V^T P^T; the
+// MFMA's K slots of that product are assigned to keys in the order in which
+// the score registers hold them (lane group g holds keys 4g..4g+3 and
+// 16+4g..16+4g+3 of every 32), and V^T is stored in global memory in that
+// order (bits 4, 3, 2 of the key index moved to bits 2, 4, 3 within each
+// group of 32 keys), so each such fragment is one 16-byte read.
 //
 // Pipeline: after the barrier of key tile i, a wave multiplies the scores of
 // tile i+1 on the matrix cores while its vector ALUs turn the scores of tile i
 // into weights, then accumulates P(i) V(i). K and V^T tiles are double
-// buffered in LDS and stream in one tile ahead through gfx950's global-to-LDS
-// loads; there is one barrier per tile.
+// buffered in LDS and stream in through gfx950's global-to-LDS loads (K two
+// tiles ahead, V one), with one barrier per tile.
 //
 // Softmax weights. The stored queries already carry the factor log2(e)/sqrt(128)
 // (the QKV epilogue applies it before rounding q to bf16), so a score
 // s = q.k is in base-2 units, and P = bf16(2^(s - m)) for an integer shift m
 // per query. The score MFMAs start their accumulation from -m, so the matrix
 // cores deliver s - m and each weight costs one exp2. m is not raised tile by
-// tile: it is set from the first tile's maximum, and afterwards only when
-// some lane's sum of its 32 new weights exceeds 2^32 is the tile's maximum
-// taken, m raised to its rounded-up value, the running output and sum
-// rescaled by the exact power of two 2^(m_old - m_new), and the tile's weights
-// formed again. Every weight is therefore at most 2^32. Because rescaling by
-// a power of two commutes with bf16 rounding, the result equals that of the
-// single shift ceil(max over all keys): o = bf16(sum P v / sum P), the sum
-// taken over the rounded weights.
+// tile: it is set to the first tile's rounded-up maximum plus 32, and the
+// running output is never rescaled. The loop only notes (in a wave-wide flag,
+// without a branch) whether some lane's sum of its 16 weights of a query in
+// some tile exceeded 2^76, i.e. a score more than about 104 above the first
+// tile's maximum. After the pass such a wave computes the exact maxima of its
+// rows (scores only, K read from global memory), and the workgroup runs the
+// whole key loop a second time, that wave's shifts raised to at least the
+// rounded-up row maxima. Every weight of the kept pass is at most 2^76.
+// Nothing in the common path touches the accumulated output outside the
+// matrix cores (a rescale of it inside the loop would not fit the registers).
+// Because scaling by a power of two commutes with bf16 rounding, the result
+// equals that of the single shift ceil(max over all keys) (up to weights more
+// than 2^94 below the largest, which may underflow): o = bf16(sum P v / sum P),
+// the sum taken over the rounded weights.
 //
 // LDS layouts: K tile [64 keys][128 dims], 256-byte rows, 16-byte chunk c
 // stored at c ^ (row & 15); V^T tile [128 dims][64 keys], 128-byte rows,
@@ -52,10 +62,17 @@ constexpr int NTHREADS = 64 * NW;  // threads per workgroup
 constexpr int KT = 64;             // keys per tile
 constexpr int K_ELEMS = KT * 128;  // bf16 elements of one K tile (16 KB)
 constexpr int V_ELEMS = 128 * KT;  // bf16 elements of one V^T tile (16 KB)
-constexpr int KSTAGE0 = 0, VSTAGE0 = 2 * K_ELEMS;  // [K0 | K1 | V0 | V1], 64 KB
-// A lane's weight sum per tile that forces a new shift. Weights up to 2^32
-// keep every fp32 sum (at most 2^20 keys) far below overflow.
-constexpr float SUM_LIMIT = 4294967296.0f;
+constexpr int VSTAGE0 = 2 * K_ELEMS;  // [K0 | K1 | V0 | V1], 64 KB
+// The first shift lies SHIFT_BIAS above the first tile's maximum, and a
+// lane's weight sum per query and tile above SUM_LIMIT forces the second pass:
+// a score more than about 104 (base 2) above the first tile's maximum. The
+// largest score of a row then has a weight in [2^-32, 2^76]; sums over up to
+// 2^20 keys stay below 2^96, and the output accumulators neither overflow nor
+// underflow for values between 2^-94 and 2^32 in size. The bias is kept small
+// because the score MFMAs accumulate s - m in fp32: the nearer s - m stays to
+// zero for the largest scores, the finer the argument of their exp2.
+constexpr float SHIFT_BIAS = 32.0f;
+constexpr float SUM_LIMIT = 75557863725914323419136.0f;  // 2^76
 
 // Wait for all of this wave's tile copies, then meet the other waves.
 __device__ __forceinline__ void tile_barrier() {
@@ -70,10 +87,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
                                                                 bf16 *__restrict__ o, int T,
                                                                 int H, int Tp) {
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * K_ELEMS + 2 * V_ELEMS];
+  __shared__ int rerun;  // some wave of the workgroup needs pass 1
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = lane >> 5, c = lane & 31;
+  const int g = lane >> 4, r = lane & 15;
+  if (tid == 0) rerun = 0;
+  __syncthreads();
   // Work order: the dispatcher hands workgroup i to XCD i % 8. The linear id
   // is remapped so that each XCD receives a contiguous range of (head, query
   // tile) items, head-major: the workgroups in flight on one XCD then work on
@@ -82,8 +102,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   int h, qt;
   {
     const int n = (int)gridDim.x, bid = (int)blockIdx.x;
-    const int xcd = bid & 7, idx = bid >> 3, q = n >> 3, r = n & 7;
-    const int L = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+    const int xcd = bid & 7, idx = bid >> 3, q = n >> 3, rem = n & 7;
+    const int L = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + idx;
     h = L / qtiles;
     qt = L - h * qtiles;
   }
@@ -92,13 +112,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   const int q0 = qt * QT + wave * 32;
   const int ntiles = (int)ceil_div(T, KT);
 
-  // this lane's query fragments: Q[q0 + c][16 s + 8 G .. +7], s = 0..7
-  bf16x8 qf[8];
-  {
-    const int qrow = min(q0 + c, T - 1);
-    const bf16 *qp = qk + (int64_t)qrow * ldqk + h * 128 + 8 * G;
+  // this lane's query fragments: Q[q0 + 16 qb + r][32 s + 8 g .. +7], s = 0..3
+  bf16x8 qf[2][4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qp + 16 * s);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = min(q0 + 16 * qb + r, T - 1);
+    const bf16 *qp = qk + (int64_t)qrow * ldqk + h * 128 + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qp + 32 * s);
   }
 
   // Tile copies: wave w fills 1 KB blocks 2w, 2w+1 of a K tile (4 rows of 256 B
@@ -108,6 +129,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   // dim row and the tile's first key (V^T).
   const bf16 *khead = qk + A + h * 128;
   const bf16 *vhead = vt + (int64_t)h * 128 * Tp;
+  const uint32_t lds0 = lds_address(lds);
   int krow[2], kcol[2];
   uint32_t kofs[2], vofs[2];
 #pragma unroll
@@ -119,9 +141,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
     const int vr = (2 * wave + j) * 8 + (lane >> 3);  // dim row of V^T
     vofs[j] = (uint32_t)(vr * Tp + ((lane & 7) ^ ((vr >> 1) & 7)) * 8) * 2u;
   }
-  const uint32_t lds0 = lds_address(lds);
   auto kload = [&](int stage, int tile) {
-    const uint32_t dst = lds0 + (uint32_t)(KSTAGE0 + stage * K_ELEMS + wave * 2 * 512) * 2u;
+    const uint32_t dst = lds0 + (uint32_t)(stage * K_ELEMS + wave * 2 * 512) * 2u;
     const bf16 *base = khead + (int64_t)tile * KT * ldqk;
     const int rows = T - tile * KT;  // keys present in this tile
     if (rows >= KT) {
@@ -141,152 +162,175 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   };
 
   // Fragment read offsets (elements) within stage 0. The swizzles depend only
-  // on the lane's row within a 16-row (K) or 32-row (V^T) group, so the other
-  // key block, the other dim blocks and the other stage are immediate offsets.
-  int koff[8];  // K row c, 16-byte chunk 2 s + G
+  // on the lane's row within a 16-row group, so the other key blocks, the other
+  // dim blocks and the other stage are immediate offsets. K: row r, 16-byte
+  // chunk (4 s + g) ^ r; V^T: row r, chunk (4 ks + g) ^ ((r >> 1) & 7) (key
+  // slots 32 ks + 8 g ..).
+  int koff[4], voff[2];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) koff[s] = KSTAGE0 + c * 128 + (((2 * s + G) ^ (c & 15)) * 8);
-  int voff[4];  // V^T row c, 16-byte chunk 2 j + G
+  for (int s = 0; s < 4; ++s) koff[s] = r * 128 + (((4 * s + g) ^ r) * 8);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) voff[j] = VSTAGE0 + c * 64 + (((2 * j + G) ^ ((c >> 1) & 7)) * 8);
+  for (int ks = 0; ks < 2; ++ks) voff[ks] = VSTAGE0 + r * 64 + (((4 * ks + g) ^ ((r >> 1) & 7)) * 8);
 
-  f32x16 oacc[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) oacc[d][v] = 0.0f;
-  float m_run = 0.0f, l_run = 0.0f;
-  f32x16 negm;  // -m_run in every element: the score MFMAs start from it
-#pragma unroll
-  for (int v = 0; v < 16; ++v) negm[v] = 0.0f;
+  f32x4 oacc[8][2];  // [dim block][query block]
+  float l_run[2];
+  f32x4 negm[2];  // -m (the shift) of each query block in every element: the score MFMAs start from it
+  float mrow[2] = {-INFINITY, -INFINITY};  // rounded-up row maxima (pass 1 of a flagged wave)
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  f32x16 sacc[2][2];  // [parity][key block]: s - m of one tile
-  u32x4 pf[4];        // P^T fragments of the four k-steps of P V
+  f32x4 sacc[2][4][2];  // [parity][key block][query block]: s - m of one tile
+  u32x4 pf[2][2];       // P^T fragments [32-key slab][query block] of P V
 
-  // S^T(tile) - m from K stage KS into sacc[KS]
-  auto scores = [&](auto ks_c) {
-    constexpr int KS = decltype(ks_c)::value;
+  // S^T(tile) - m from K stage KS into sacc[D]
+  auto scores = [&](auto ks_c, auto d_c) {
+    constexpr int KS = decltype(ks_c)::value, D = decltype(d_c)::value;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
+      for (int b = 0; b < 4; ++b) {
         const bf16x8 kf =
-            *reinterpret_cast<const bf16x8 *>(lds + koff[s] + b * 32 * 128 + KS * K_ELEMS);
-        sacc[KS][b] = mfma32(kf, qf[s], s == 0 ? negm : sacc[KS][b]);
+            *reinterpret_cast<const bf16x8 *>(lds + KS * K_ELEMS + koff[s] + b * 16 * 128);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[D][b][qb] = mfma16(kf, qf[qb][s], s == 0 ? negm[qb] : sacc[D][b][qb]);
       }
   };
 
-  // P = bf16(2^(sacc - dm)) straight into the P^T fragments (fragment j holds
-  // registers 8 (j % 2) .. +7 of score block j / 2); returns this lane's sum
-  // of its 32 weights.
-  auto weights = [&](auto p_c, float dm) -> float {
-    constexpr int P = decltype(p_c)::value;
-    float t[2] = {0.0f, 0.0f};
+  // The same product with the K rows of tile `tile` read from global memory
+  // (its LDS stage is being refilled by then); only the rare path uses it.
+  auto scores_global = [&](int tile, auto d_c) {
+    constexpr int D = decltype(d_c)::value;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b) {
+      const int row = min(tile * KT + 16 * b + r, T - 1);
+      const bf16 *kp = khead + (int64_t)row * ldqk + 8 * g;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float p0 = __builtin_amdgcn_exp2f(sacc[P][b][2 * u] - dm);
-        const float p1 = __builtin_amdgcn_exp2f(sacc[P][b][2 * u + 1] - dm);
-        const bf16x2 pr = pack2(p0, p1);
-        pf[2 * b + (u >> 2)][u & 3] = __builtin_bit_cast(uint32_t, pr);
-        t[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, t[u & 1], false);
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[D][b][qb] = mfma16(kf, qf[qb][s], s == 0 ? negm[qb] : sacc[D][b][qb]);
       }
-    return t[0] + t[1];
+    }
+  };
+
+  // keys past T of tile `tile` get zero weight
+  auto mask = [&](auto d_c, int tile) {
+    constexpr int D = decltype(d_c)::value;
+    const int kv0 = tile * KT;
+    if (kv0 + KT > T) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (kv0 + 16 * b + 4 * g + v >= T) sacc[D][b][qb][v] = -INFINITY;
+    }
+  };
+
+  // Largest score of each query in sacc[D] (over the whole tile: xor 16, 32
+  // reach the other three lanes of the query), rounded up.
+  auto tile_max = [&](auto d_c, int qb) -> float {
+    constexpr int D = decltype(d_c)::value;
+    float mx = sacc[D][0][qb][0];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, sacc[D][b][qb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    return ceilf(mx);
+  };
+
+  // P = bf16(2^sacc[P]) straight into the P^T fragments (fragment [ks][qb]
+  // holds key blocks 2 ks and 2 ks + 1 of query block qb); t[qb] receives this
+  // lane's sum of its 16 weights of query block qb.
+  auto weights = [&](auto p_c, float t[2]) {
+    constexpr int P = decltype(p_c)::value;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float tq[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[P][b][qb][2 * u]);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[P][b][qb][2 * u + 1]);
+          const bf16x2 pr = pack2(p0, p1);
+          pf[b >> 1][qb][2 * (b & 1) + u] = __builtin_bit_cast(uint32_t, pr);
+          tq[u] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, tq[u], false);
+        }
+      t[qb] = tq[0] + tq[1];
+    }
   };
 
   // O^T[dim][query] += V^T[dim][keys] P^T[keys][query] from V stage VS
   auto pv = [&](auto vs_c) {
     constexpr int VS = decltype(vs_c)::value;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 pj = __builtin_bit_cast(bf16x8, pf[j]);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 8; ++db) {
         const bf16x8 vf =
-            *reinterpret_cast<const bf16x8 *>(lds + voff[j] + VS * V_ELEMS + db * 32 * 64);
-        oacc[db] = mfma32(vf, pj, oacc[db]);
+            *reinterpret_cast<const bf16x8 *>(lds + voff[ks] + VS * V_ELEMS + db * 16 * 64);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          oacc[db][qb] = mfma16(vf, __builtin_bit_cast(bf16x8, pf[ks][qb]), oacc[db][qb]);
       }
-    }
-    // fragment reads run four MFMAs ahead of their use
+    // fragment reads run four reads (eight MFMAs) ahead of their use
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int k = 0; k < 12; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
-  // One tile: copies of K(it + 2) and V(it + 1), S(it + 1) (when NEXT_S)
-  // overlapped with the weights of tile it, the shift check, then P V.
-  auto step = [&](auto p_c, auto next_s_c, int it) {
+  // One tile (stages P = it % 2): copies of K(it + 2) into the K stage of
+  // tile it (its scores were multiplied in the previous step) and of V(it + 1)
+  // into the V stage of tile it - 1 (last read before this barrier), S(it + 1)
+  // (when NEXT_S) overlapped with the weights of tile it, the shift check,
+  // then P V.
+  auto step = [&](auto p_c, auto next_s_c, int it, bool &again) {
     constexpr int P = decltype(p_c)::value;
     constexpr bool NEXT_S = decltype(next_s_c)::value;
-    using KN = std::integral_constant<int, P ^ 1>;
+    using DC = std::integral_constant<int, P>;
+    using DN = std::integral_constant<int, P ^ 1>;
     tile_barrier();  // V(it) and K(it + 1) are in LDS everywhere
     if (it + 2 < ntiles) kload(P, it + 2);
     if (it + 1 < ntiles) vload(P ^ 1, it + 1);
 
-    const int kv0 = it * KT;
-    if (kv0 + KT > T) {  // ragged last tile: keys past T get zero weight
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kv0 + 32 * b + 8 * (v >> 2) + 4 * G + (v & 3);
-          if (key >= T) sacc[P][b][v] = -INFINITY;
-        }
-    }
-
-    if constexpr (NEXT_S) scores(KN());
-    float ts = weights(p_c, 0.0f);
+    mask(DC(), it);
+    if constexpr (NEXT_S) scores(DN(), DN());
+    float ts[2];
+    weights(p_c, ts);
     if constexpr (NEXT_S) {
       // score MFMAs interleaved with the weight computation, K fragment reads
-      // running four MFMAs ahead
+      // running four reads ahead
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int k = 0; k < 12; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
     }
 
-    // First tile: take the shift from its maximum. Later tiles: only when the
-    // weights grew past 2^32 (or overflowed).
-    if (__ballot((ts > SUM_LIMIT) | (it == 0))) {
-      float mx = fmaxf(sacc[P][0][0], sacc[P][1][0]);
-#pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(sacc[P][0][v], sacc[P][1][v]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float dm = ceilf(mx);  // integer step of the shift
-      if (it > 0) {
-        dm = fmaxf(dm, 0.0f);
-        const float fct = __builtin_amdgcn_exp2f(-dm);  // exact power of two
-        l_run *= fct;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[d][v] *= fct;
-      }
-      m_run += dm;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) negm[v] = -m_run;
-      if constexpr (NEXT_S) {  // the next tile's scores were taken with the old shift
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sacc[P ^ 1][b][v] -= dm;
-      }
-      ts = weights(p_c, dm);
-    }
-    l_run += ts;
+    // Weights grew past 2^76 (or overflowed): the row maxima are found after
+    // this pass and the pass is run again (rare; no branch here).
+    again |= __ballot((ts[0] > SUM_LIMIT) | (ts[1] > SUM_LIMIT)) != 0;
+    l_run[0] += ts[0];
+    l_run[1] += ts[1];
     pv(p_c);
   };
 
@@ -295,38 +339,90 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   using Y = std::true_type;
   using N = std::false_type;
 
-  // prologue: K(0), K(1), V(0) in flight; S(0) once they land
-  kload(0, 0);
-  if (ntiles > 1) kload(1, 1);
-  vload(0, 0);
-  tile_barrier();
-  scores(I0());
+  // Pass 0 takes the shift from the first tile's maximum (plus SHIFT_BIAS).
+  // If some tile's weights outgrow 2^76, the wave finds the exact maxima of
+  // its rows and pass 1 runs the whole key loop again with the shift at
+  // least ceil(row maximum): no weight exceeds 1 and nothing fires.
+  for (int pass = 0;; ++pass) {
+    bool again = false;
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) oacc[d][qb][v] = 0.0f;
+    l_run[0] = l_run[1] = 0.0f;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) negm[qb][v] = 0.0f;
 
-  int it = 0;
-  for (; it + 2 < ntiles; it += 2) {
-    step(I0(), Y(), it);
-    step(I1(), Y(), it + 1);
-  }
-  if (ntiles - it == 2) {
-    step(I0(), Y(), it);
-    step(I1(), N(), it + 1);
-  } else {
-    step(I0(), N(), it);
-  }
+    // prologue: K(0), K(1), V(0) in flight; S(0) once they land, and the
+    // shift from its maximum
+    kload(0, 0);
+    if (ntiles > 1) kload(1, 1);
+    vload(0, 0);
+    tile_barrier();
+    scores(I0(), I0());
+    mask(I0(), 0);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m = fmaxf(tile_max(I0(), qb) + SHIFT_BIAS, mrow[qb]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) negm[qb][v] = -m;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sacc[0][b][qb][v] -= m;
+    }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const int q = q0 + c;
-  if (q < T) {
-    bf16 *op = o + (int64_t)q * A + h * 128 + 4 * G;
+    int it = 0;
+    for (; it + 2 < ntiles; it += 2) {
+      step(I0(), Y(), it, again);
+      step(I1(), Y(), it + 1, again);
+    }
+    if (ntiles - it == 2) {
+      step(I0(), Y(), it, again);
+      step(I1(), N(), it + 1, again);
+    } else {
+      step(I0(), N(), it, again);
+    }
+    if (pass == 1) break;
+    if (again) {
+      // exact row maxima of this wave's queries, K read from global memory
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 r;
+        for (int v = 0; v < 4; ++v) negm[qb][v] = 0.0f;
+      for (int t = 0; t < ntiles; ++t) {
+        scores_global(t, I0());
+        mask(I0(), t);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = to_bf16(oacc[db][4 * g + e] / l_tot);
-        *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * g) = r;
+        for (int qb = 0; qb < 2; ++qb) mrow[qb] = fmaxf(mrow[qb], tile_max(I0(), qb));
       }
+    }
+    // the workgroup runs pass 1 if any of its waves needs it (every wave
+    // takes part in the tile copies and barriers)
+    if (again && lane == 0) rerun = 1;
+    __syncthreads();
+    if (!rerun) break;
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    const int q = q0 + 16 * qb + r;
+    if (q < T) {
+      bf16 *op = o + (int64_t)q * A + h * 128 + 4 * g;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        bf16x4 rv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rv[e] = to_bf16(oacc[db][qb][e] / l_tot);
+        *reinterpret_cast<bf16x4 *>(op + db * 16) = rv;
+      }
+    }
   }
 }
 

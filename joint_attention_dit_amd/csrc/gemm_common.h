@@ -82,9 +82,12 @@ __device__ __forceinline__ bf16x4 gelu4(float v0, float v1, float v2, float v3) 
   return r;
 }
 
-// token t of a V tile is stored at column t with bits 2 and 3 exchanged (the key
-// order of the attention kernel's P V fragments)
-__device__ __forceinline__ int vt_col(int t) { return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1); }
+// token t of a V tile is stored at column vt_col(t): bits 4, 3, 2 of t move to
+// bits 2, 4, 3, a permutation within each group of 32 keys (the key order of
+// the attention kernel's P V fragments)
+__device__ __forceinline__ int vt_col(int t) {
+  return (t & ~28) | ((t & 12) << 1) | ((t & 16) >> 2);
+}
 
 // Four consecutive outputs (features n .. n+3 of token t) through the epilogue.
 template <int EPI>

@@ -187,8 +187,8 @@ def test_block_mxfp8_deterministic_and_weights_unchanged():
 
 
 def _unswap_vt(vt):
-    cols = np.arange(vt.shape[-1])
-    return vt[..., (cols & ~12) | ((cols & 4) << 1) | ((cols & 8) >> 1)]
+    t = np.arange(vt.shape[-1])
+    return vt[..., (t & ~28) | ((t & 12) << 1) | ((t & 16) >> 2)]
 
 
 def _check_linear(got, resid, gate, xd, wd, what, post=None):

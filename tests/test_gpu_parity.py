@@ -44,9 +44,10 @@ def f64_dev(a: np.ndarray):
 
 
 def unswap_vt(vt):
-    """vt columns hold token t at t with bits 2 and 3 exchanged; undo that."""
-    cols = np.arange(vt.shape[-1])
-    src = (cols & ~12) | ((cols & 4) << 1) | ((cols & 8) >> 1)
+    """vt holds token t in column t with bits 4, 3, 2 moved to bits 2, 4, 3
+    (a permutation within each group of 32 keys); return it in token order."""
+    t = np.arange(vt.shape[-1])
+    src = (t & ~28) | ((t & 12) << 1) | ((t & 16) >> 2)
     return vt[..., src]
 
 
@@ -171,6 +172,70 @@ def test_attention_single_token_returns_v():
     o = torch.empty(1, 256, dtype=torch.bfloat16, device="cuda")
     B.h3dit_attention(c, qk, vt, o)
     assert torch.equal(o.cpu(), vt[:, :, 0].reshape(1, 256).cpu())
+
+
+def _vt_from_tokens(v: torch.Tensor, Tp: int) -> torch.Tensor:
+    """[T, H, 128] values -> [H, 128, Tp] in the kernel's column order."""
+    T, H, _ = v.shape
+    vt = torch.zeros(H, 128, Tp, dtype=v.dtype)
+    t = np.arange(T)
+    cols = (t & ~28) | ((t & 12) << 1) | ((t & 16) >> 2)
+    vt[:, :, torch.from_numpy(cols)] = v.permute(1, 2, 0)
+    return vt
+
+
+@pytest.mark.parametrize("case", ["planted", "ramp"])
+def test_attention_shift_rise(case):
+    """Scores far above the first key tile's maximum force the rise of the
+    shift (the kernel runs the key loop again with the raised shift): planted
+    keys in an early, a middle and the ragged last tile for queries of
+    different workgroups, or keys whose norm grows along the sequence so that
+    every row's maximum lies far past its first tile (weights of the first
+    pass overflow). The oracle takes the single shift ceil(max s) per row."""
+    T, H = 700, 2
+    say(f"[stage] attention shift rise {case} T={T} H={H}")
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(T, H, 128, generator=g) * 0.5
+    k = torch.randn(T, H, 128, generator=g) * 0.5   # scores ~N(0, 2.8^2), base 2
+    if case == "planted":
+        for qi, ki in ((5, 100), (300, 650), (520, 695), (699, 64)):
+            for h in range(H):
+                k[ki, h] = q[qi, h] * (160.0 / float(q[qi, h].square().sum()))
+    else:
+        k *= (0.2 + 40.0 * torch.arange(T, dtype=torch.float32) / T).reshape(T, 1, 1)
+    v = torch.randn(T, H, 128, generator=g)
+    qb, kb, vb = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    Tp = B.h3dit_padded_tokens(T)
+    qk = torch.cat([qb.reshape(T, H * 128), kb.reshape(T, H * 128)], dim=1).contiguous().cuda()
+    vt = _vt_from_tokens(vb, Tp).cuda()
+    o = torch.empty(T, H * 128, dtype=torch.bfloat16, device="cuda")
+    cfg = small_config("shift", hidden=256, heads=H, ffn=256, text_tokens=T, images=())
+    B.h3dit_attention(B.config_from(cfg), qk, vt, o)
+    f = lambda t: t.to(torch.float64).numpy()
+    s_max = max(float((f(qb)[:, h] @ f(kb)[:, h].T).max()) for h in range(H))
+    first = max(float((f(qb)[:, h] @ f(kb)[:64, h].T).max()) for h in range(H))
+    say(f"  max score {s_max:.1f}, first tile max {first:.1f}")
+    assert s_max > first + 130, "the case must push scores far past the first tile"
+    ref = O.attention(f(qb), f(kb), f(vb), "contract").reshape(T, H * 128)
+    got = host(o)
+    e = errors(got, ref)
+    say(f"  o: rel_l2 {e['rel_l2']:.2e}")
+    assert np.all(np.isfinite(got))
+    assert e["rel_l2"] < 1e-3
+    # Per element: two bf16 ulps of the output, plus what a one-ulp difference
+    # in any weight's bf16 rounding (fp32 scores on the GPU, fp64 in the
+    # oracle) moves: |dP_i| <= 2^-7 P_i, so |do| <= 2^-7 (sum P_i |v_i| / sum P
+    # + |o|). Peaked rows with cancelling values need that second term.
+    flip = np.empty_like(ref)
+    for h in range(H):
+        sc = f(qb)[:, h] @ f(kb)[:, h].T
+        P = O.bf16_round(np.exp2(sc - np.ceil(sc.max(axis=1, keepdims=True))))
+        flip[:, h * 128:(h + 1) * 128] = (P @ np.abs(f(vb)[:, h])) / P.sum(axis=1, keepdims=True)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bound = 2 * 2.0 ** -7 * np.abs(ref) + 2.0 ** -7 * (flip + np.abs(ref)) + 1e-4 * rms
+    excess = np.abs(got - ref) / bound
+    say(f"  o: max err/bound {excess.max():.3f}, mismatch fraction {np.mean(got != ref):.2e}")
+    assert excess.max() <= 1.0
 
 
 @pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
