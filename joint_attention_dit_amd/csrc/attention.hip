@@ -306,23 +306,16 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
     float ts[2];
     weights(p_c, ts);
     if constexpr (NEXT_S) {
-      // score MFMAs interleaved with the weight computation, K fragment reads
-      // running four reads ahead
+      // score MFMAs interleaved with the weight computation (three, then two
+      // VALU instructions after each), K fragment reads running four ahead
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int k = 0; k < 12; ++k) {
+      for (int k = 0; k < 16; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
     }
 
@@ -412,6 +405,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   for (int qb = 0; qb < 2; ++qb) {
     float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
+    const float inv_l = 1.0f / l_tot;  // one division per row, 64 products
     const int q = q0 + 16 * qb + r;
     if (q < T) {
       bf16 *op = o + (int64_t)q * A + h * 128 + 4 * g;
@@ -419,7 +413,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
       for (int db = 0; db < 8; ++db) {
         bf16x4 rv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rv[e] = to_bf16(oacc[db][qb][e] / l_tot);
+        for (int e = 0; e < 4; ++e) rv[e] = to_bf16(oacc[db][qb][e] * inv_l);
         *reinterpret_cast<bf16x4 *>(op + db * 16) = rv;
       }
     }
