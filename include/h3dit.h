@@ -23,8 +23,12 @@
  * normalisations are computed in fp64; x1 and the output are fp32. The
  * stored query carries the softmax factor: q = bf16(rope(q) * log2(e)/sqrt(128)),
  * rounded once, so a score s = q.k is a base-2 exponent; the attention
- * weights are bf16(2^(s - m)) for an integer shift m per query (the rounded-up
- * maximum score), normalised by their own sum.
+ * weights are bf16(2^(s - m)) for an integer shift m per query, normalised by
+ * their own sum. Since scaling by a power of two commutes with the rounding,
+ * the result is that of m = the rounded-up maximum score for values of
+ * magnitude 2^-94..2^32 (the kernel takes the first key tile's rounded-up
+ * maximum plus 32, or the exact one when a weight would exceed about 2^72;
+ * weights more than 2^94 below a row's largest may underflow to zero).
  *
  * Memory: every pointer argument is a DEVICE pointer unless marked (host);
  * matrices are row-major and dense; the caller owns all memory, including the
