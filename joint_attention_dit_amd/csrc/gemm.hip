@@ -174,7 +174,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
       }
       fa[i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + i * 16 * BK);
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
