@@ -2,7 +2,8 @@
 // (model card, "Model Architecture": every token sits in one packed sequence
 // of a single-stream transformer; spec page: 56 query and 56 key-value heads
 // of dimension 128). Flash-style: keys and values are visited in tiles of 64
-// with an online softmax, so no T x T matrix is ever stored.
+// and the weights are accumulated as they are formed (one integer shift per
+// row, below), so no T x T matrix is ever stored.
 //
 // Work split: a workgroup owns 256 queries of one head (eight waves of 32, two
 // waves per SIMD). Each wave computes the transposed score tile S^T = K Q^T
