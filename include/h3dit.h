@@ -252,6 +252,14 @@ size_t h3dit_mxfp8_scale_bytes(int64_t rows, int64_t K);
 int h3dit_mxfp8_quantize(const void *x, int64_t rows, int64_t K, uint8_t *codes,
                          uint8_t *scales, void *stream);
 
+/* Step 5 for the MXFP8 output projection (vLLM blog "H3-Image Day-0
+ * Support", section Inference Optimizations: the DiT linears in MXFP8):
+ * h3dit_attention (same o, bitwise), and in the same pass o's MXFP8 codes
+ * [T, A] and scales (layout above, h3dit_mxfp8_scale_bytes(T, A) bytes),
+ * bitwise equal to h3dit_mxfp8_quantize of that o. */
+int h3dit_attention_mxfp8(const h3dit_config *cfg, const void *qk, const void *vt, void *o,
+                          uint8_t *o_codes, uint8_t *o_scales, void *stream);
+
 /* y[M, N] fp32 = X . W^T for MXFP8 operands X [M, K] and W [N, K] (codes +
  * scales as above), fp32 accumulation in the matrix cores' scaled E4M3
  * product. N % 4 == 0, K a multiple of 128. */

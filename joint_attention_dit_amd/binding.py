@@ -31,7 +31,7 @@ EXPORTED = (
     "h3dit_dit_forward_mod", "h3dit_mxfp8_scale_bytes", "h3dit_mxfp8_quantize",
     "h3dit_linear_mxfp8", "h3dit_workspace_size_mxfp8", "h3dit_block_forward_mxfp8",
     "h3dit_block_forward_mxfp8_timed", "h3dit_workspace_layout", "h3dit_stack_workspace_size_mxfp8",
-    "h3dit_dit_forward_mxfp8", "h3dit_dit_forward_mod_mxfp8",
+    "h3dit_dit_forward_mxfp8", "h3dit_dit_forward_mod_mxfp8", "h3dit_attention_mxfp8",
 )
 
 
@@ -114,6 +114,7 @@ def load_library() -> ctypes.CDLL:
         "h3dit_dit_forward_mod": [cfgp, ctypes.POINTER(StackConfig), ctypes.POINTER(StackWeights),
                                   vp, vp, vp, vp, vp, vp, sz, vp],
         "h3dit_mxfp8_quantize": [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp],
+        "h3dit_attention_mxfp8": [cfgp, vp, vp, vp, vp, vp, vp],
         "h3dit_linear_mxfp8": [vp, vp, vp, vp, i32, i32, i32, vp, vp],
         "h3dit_workspace_size_mxfp8": [cfgp, ctypes.POINTER(sz)],
         "h3dit_workspace_layout": [cfgp, i32, ctypes.POINTER(WorkspaceMap)],
@@ -255,6 +256,12 @@ def h3dit_qkv_rope(cfg: Config, h, w_qkv, table, qk, vt, stream=None) -> None:
 def h3dit_attention(cfg: Config, qk, vt, o, stream=None) -> None:
     _check(load_library().h3dit_attention(ctypes.byref(cfg), _ptr(qk), _ptr(vt), _ptr(o),
                                           _stream(stream)), "h3dit_attention")
+
+
+def h3dit_attention_mxfp8(cfg: Config, qk, vt, o, o_codes, o_scales, stream=None) -> None:
+    _check(load_library().h3dit_attention_mxfp8(ctypes.byref(cfg), _ptr(qk), _ptr(vt), _ptr(o),
+                                                _ptr(o_codes), _ptr(o_scales), _stream(stream)),
+           "h3dit_attention_mxfp8")
 
 
 def h3dit_out_proj_residual(cfg: Config, o, w_o, resid, gate, x1, stream=None) -> None:

@@ -50,6 +50,7 @@
 // chunk c at c ^ ((row >> 1) & 7). Both make the fragment reads conflict-free.
 #include "common.h"
 #include "kernels.h"
+#include "mxfp8_device.h"
 
 #include <type_traits>
 
@@ -83,10 +84,15 @@ __device__ __forceinline__ void tile_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// With MX, o is also written as MXFP8 codes [T, A] and scales (the layout of
+// mxfp8_quantize_kernel), the operand of the MXFP8 output projection.
+template <bool MX>
 __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__restrict__ qk,
                                                                 const bf16 *__restrict__ vt,
-                                                                bf16 *__restrict__ o, int T,
-                                                                int H, int Tp) {
+                                                                bf16 *__restrict__ o,
+                                                                uint8_t *__restrict__ o_codes,
+                                                                uint8_t *__restrict__ o_scales,
+                                                                int T, int H, int Tp) {
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * K_ELEMS + 2 * V_ELEMS];
   __shared__ int rerun;  // some wave of the workgroup needs pass 1
 
@@ -408,14 +414,44 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
     l_tot += __shfl_xor(l_tot, 32, 64);
     const float inv_l = 1.0f / l_tot;  // one division per row, 64 products
     const int q = q0 + 16 * qb + r;
+    bf16x4 rv[8];  // dims 16 db + 4 g .. +3 of query q
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rv[db][e] = to_bf16(oacc[db][qb][e] * inv_l);
     if (q < T) {
       bf16 *op = o + (int64_t)q * A + h * 128 + 4 * g;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        bf16x4 rv;
+      for (int db = 0; db < 8; ++db) *reinterpret_cast<bf16x4 *>(op + db * 16) = rv[db];
+    }
+    if constexpr (MX) {
+      // MX block j = dims 32 j .. 32 j + 31 of the head: dim blocks 2 j and
+      // 2 j + 1 of the four lanes l ^ 16, l ^ 32 that hold query q
 #pragma unroll
-        for (int e = 0; e < 4; ++e) rv[e] = to_bf16(oacc[db][qb][e] * inv_l);
-        *reinterpret_cast<bf16x4 *>(op + db * 16) = rv;
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 w0 = __builtin_bit_cast(u32x2, rv[2 * j]);
+        const u32x2 w1 = __builtin_bit_cast(u32x2, rv[2 * j + 1]);
+        uint32_t amax = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          amax = max(amax, max(w0[e] & 0x7FFFu, (w0[e] >> 16) & 0x7FFFu));
+          amax = max(amax, max(w1[e] & 0x7FFFu, (w1[e] >> 16) & 0x7FFFu));
+        }
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 16, 64));
+        amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32, 64));
+        const int sbyte = mx_scale_byte(amax);
+        const float inv = mx_inv_scale(sbyte);
+        if (q < T) {
+          uint8_t *cp = o_codes + (int64_t)q * A + h * 128 + 32 * j + 4 * g;
+          *reinterpret_cast<uint32_t *>(cp) =
+              mx_code4(mx_bf16_value(w0[0] & 0xFFFFu), mx_bf16_value(w0[0] >> 16),
+                       mx_bf16_value(w0[1] & 0xFFFFu), mx_bf16_value(w0[1] >> 16), inv);
+          *reinterpret_cast<uint32_t *>(cp + 16) =
+              mx_code4(mx_bf16_value(w1[0] & 0xFFFFu), mx_bf16_value(w1[0] >> 16),
+                       mx_bf16_value(w1[1] & 0xFFFFu), mx_bf16_value(w1[1] >> 16), inv);
+        }
+        // rows past T of the last 256-row panel get scale byte 0
+        if (g == 0) o_scales[mx_scale_offset(q, 4 * h + j, A)] = (uint8_t)(q < T ? sbyte : 0);
       }
     }
   }
@@ -426,8 +462,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
                             hipStream_t s) {
   dim3 grid((unsigned)(ceil_div(T, QT) * H));
-  hipLaunchKernelGGL(attention_kernel, grid, dim3(NTHREADS), 0, s, static_cast<const bf16 *>(qk),
-                     static_cast<const bf16 *>(vt), static_cast<bf16 *>(o), T, H, Tp);
+  hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(NTHREADS), 0, s,
+                     static_cast<const bf16 *>(qk), static_cast<const bf16 *>(vt),
+                     static_cast<bf16 *>(o), nullptr, nullptr, T, H, Tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_mx(const void *qk, const void *vt, void *o, uint8_t *o_codes,
+                               uint8_t *o_scales, int T, int H, int Tp, hipStream_t s) {
+  dim3 grid((unsigned)(ceil_div(T, QT) * H));
+  hipLaunchKernelGGL(attention_kernel<true>, grid, dim3(NTHREADS), 0, s,
+                     static_cast<const bf16 *>(qk), static_cast<const bf16 *>(vt),
+                     static_cast<bf16 *>(o), o_codes, o_scales, T, H, Tp);
   return hipGetLastError();
 }
 

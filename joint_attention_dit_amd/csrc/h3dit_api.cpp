@@ -274,7 +274,10 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
            "qkv gemm");
   }
   LAUNCH(mark(4), "event record");
-  LAUNCH(launch_attention(qk, vt, o, T, H, (int)p.Tp, s), "attention");
+  if (q)  // o in bf16 and as MXFP8 codes for the output projection
+    LAUNCH(launch_attention_mx(qk, vt, o, qa, qas, T, H, (int)p.Tp, s), "attention");
+  else
+    LAUNCH(launch_attention(qk, vt, o, T, H, (int)p.Tp, s), "attention");
   LAUNCH(mark(5), "event record");
   {
     GemmArgs g = gemm_args(o, w->w_o, T, D, A);
@@ -282,7 +285,7 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     g.resid = x;
     g.gate = mod + 2 * D;
     LAUNCH(linear(cfg->x_dtype == H3DIT_F32 ? EPI_RESID_F32 : EPI_RESID_BF16, g,
-                  q ? q->w_o : nullptr, q ? q->w_o_scale : nullptr, qa, qas, true),
+                  q ? q->w_o : nullptr, q ? q->w_o_scale : nullptr, qa, qas, false),
            "output projection");
   }
   LAUNCH(mark(6), "event record");
@@ -690,6 +693,21 @@ int h3dit_attention(const h3dit_config *cfg, const void *qk, const void *vt, voi
   CHECK_PTR(o);
   LAUNCH(launch_attention(qk, vt, o, cfg->n_tokens, cfg->heads,
                           (int)h3dit_padded_tokens(cfg->n_tokens), static_cast<hipStream_t>(stream)),
+         "attention");
+  return ok();
+}
+
+int h3dit_attention_mxfp8(const h3dit_config *cfg, const void *qk, const void *vt, void *o,
+                          uint8_t *o_codes, uint8_t *o_scales, void *stream) {
+  CHECK_CFG(cfg);
+  CHECK_PTR(qk);
+  CHECK_PTR(vt);
+  CHECK_PTR(o);
+  CHECK_PTR(o_codes);
+  CHECK_PTR(o_scales);
+  LAUNCH(launch_attention_mx(qk, vt, o, o_codes, o_scales, cfg->n_tokens, cfg->heads,
+                             (int)h3dit_padded_tokens(cfg->n_tokens),
+                             static_cast<hipStream_t>(stream)),
          "attention");
   return ok();
 }

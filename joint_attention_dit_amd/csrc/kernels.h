@@ -89,6 +89,9 @@ hipError_t launch_mxfp8_quantize(const void *x, int rows, int K, uint8_t *codes,
 // o[T, A] = attention over qk [T, 2A] and vt [H, 128, Tp]
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
                             hipStream_t s);
+// The same, o also as MXFP8 codes [T, H * 128] and scales (mxfp8_quantize layout).
+hipError_t launch_attention_mx(const void *qk, const void *vt, void *o, uint8_t *o_codes,
+                               uint8_t *o_scales, int T, int H, int Tp, hipStream_t s);
 
 // ---- DiT stack (patch-embed, final layer, latent update) ----
 

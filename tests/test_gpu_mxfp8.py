@@ -186,6 +186,37 @@ def test_block_mxfp8_deterministic_and_weights_unchanged():
         assert torch.equal(c, blk.mx[k]) and torch.equal(s, blk.mx[k + "_scale"])
 
 
+@pytest.mark.parametrize("T,H", [(1, 1), (288, 2), (700, 3)])
+def test_attention_mxfp8_codes_bit_exact(T, H):
+    """The attention kernel's MXFP8 epilogue (o's codes for the MXFP8 output
+    projection): o bitwise equal to h3dit_attention's, codes and scales bitwise
+    equal to h3dit_mxfp8_quantize of that o, including the zero scale bytes of
+    the last panel's rows past T. V is scaled per dimension by 2^-20..2^20 so
+    that the blocks of 32 take many scale bytes."""
+    say(f"[mxfp8] attention epilogue codes T={T} H={H}")
+    A = H * 128
+    Tp = B.h3dit_padded_tokens(T)
+    g = torch.Generator().manual_seed(1000 + T + H)
+    qk = (torch.randn(T, 2 * A, generator=g) * 0.4).to(torch.bfloat16).cuda()
+    dim_scale = torch.exp2(torch.arange(128, dtype=torch.float32) % 41 - 20.0)
+    vt = (torch.randn(H, 128, Tp, generator=g) * dim_scale.reshape(1, 128, 1)).to(torch.bfloat16)
+    vt = vt.cuda()
+    cfg = B.make_config(256, H, 256, T)
+    o1 = torch.empty(T, A, dtype=torch.bfloat16, device="cuda")
+    B.h3dit_attention(cfg, qk, vt, o1)
+    o2 = torch.empty_like(o1)
+    codes = torch.empty(T, A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((B.h3dit_mxfp8_scale_bytes(T, A),), 77, dtype=torch.uint8, device="cuda")
+    B.h3dit_attention_mxfp8(cfg, qk, vt, o2, codes, scales)
+    rc, rs = B.mxfp8_quantize(o1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2), "o differs from h3dit_attention"
+    nc = int((codes != rc).sum())
+    ns = int((scales != rs).sum())
+    say(f"  codes differ: {nc}, scale bytes differ: {ns} of {scales.numel()}")
+    assert nc == 0 and ns == 0
+
+
 def _unswap_vt(vt):
     t = np.arange(vt.shape[-1])
     return vt[..., (t & ~28) | ((t & 12) << 1) | ((t & 16) >> 2)]
