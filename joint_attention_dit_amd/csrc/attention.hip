@@ -419,7 +419,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int e = 0; e < 4; ++e) rv[db][e] = to_bf16(oacc[db][qb][e] * inv_l);
-    if (q < T) {
+    if (q < T && (!MX || o)) {  // with MX, o may be left out (only its codes consumed)
       bf16 *op = o + (int64_t)q * A + h * 128 + 4 * g;
 #pragma unroll
       for (int db = 0; db < 8; ++db) *reinterpret_cast<bf16x4 *>(op + db * 16) = rv[db];

@@ -162,9 +162,11 @@ __device__ __forceinline__ void gelu_mx_block(const GemmArgs &a, int t, int n, i
   const float inv = mx_inv_scale(sbyte);
   if (t >= a.M || n >= a.N) return;
   const int64_t off = (int64_t)t * a.N + n;
-  bf16 *u = static_cast<bf16 *>(a.out);
-  *reinterpret_cast<bf16x4 *>(u + off) = g0;
-  *reinterpret_cast<bf16x4 *>(u + off + 16) = g1;
+  if (a.out) {  // the bf16 copy of u (left out when only the codes are consumed)
+    bf16 *u = static_cast<bf16 *>(a.out);
+    *reinterpret_cast<bf16x4 *>(u + off) = g0;
+    *reinterpret_cast<bf16x4 *>(u + off + 16) = g1;
+  }
   *reinterpret_cast<uint32_t *>(a.out_codes + off) =
       mx_code4((float)g0[0], (float)g0[1], (float)g0[2], (float)g0[3], inv);
   *reinterpret_cast<uint32_t *>(a.out_codes + off + 16) =

@@ -164,7 +164,9 @@ GemmArgs gemm_args(const void *x, const void *w, int64_t M, int64_t N, int64_t K
 int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, const h3dit_weights *w,
                  const int32_t *positions, float *out, void *ws, size_t ws_bytes, void *stream,
                  void *const *events, int n_events, const double *mod_in = nullptr,
-                 const h3dit_mxfp8_weights *q = nullptr) {
+                 const h3dit_mxfp8_weights *q = nullptr, bool lean = false) {
+  // lean (MXFP8 only): the producers write only the codes the next linear
+  // consumes, not the bf16 copies of h1, o, h2 and u kept for inspection
   CHECK_CFG(cfg);
   if (!w) return fail(H3DIT_EINVAL, "w is NULL");
   CHECK_PTR(x);
@@ -255,7 +257,7 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   LAUNCH(mark(2), "event record");
   if (q)  // h1 in bf16 and as MXFP8 codes for the QKV linear
     LAUNCH(launch_rmsnorm_modulate_mx(x, cfg->x_dtype == H3DIT_F32, mod + 0 * D, mod + 1 * D, h, qa,
-                                      qas, T, D, cfg->eps, s),
+                                      qas, T, D, cfg->eps, s, !lean),
            "rmsnorm 1");
   else
     LAUNCH(launch_rmsnorm_modulate(x, cfg->x_dtype == H3DIT_F32, mod + 0 * D, mod + 1 * D, h, T,
@@ -275,7 +277,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   }
   LAUNCH(mark(4), "event record");
   if (q)  // o in bf16 and as MXFP8 codes for the output projection
-    LAUNCH(launch_attention_mx(qk, vt, o, qa, qas, T, H, (int)p.Tp, s), "attention");
+    LAUNCH(launch_attention_mx(qk, vt, lean ? nullptr : o, qa, qas, T, H, (int)p.Tp, s),
+           "attention");
   else
     LAUNCH(launch_attention(qk, vt, o, T, H, (int)p.Tp, s), "attention");
   LAUNCH(mark(5), "event record");
@@ -291,7 +294,7 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   LAUNCH(mark(6), "event record");
   if (q)
     LAUNCH(launch_rmsnorm_modulate_mx(x1, true, mod + 3 * D, mod + 4 * D, h, qa, qas, T, D,
-                                      cfg->eps, s),
+                                      cfg->eps, s, !lean),
            "rmsnorm 2");
   else
     LAUNCH(launch_rmsnorm_modulate(x1, true, mod + 3 * D, mod + 4 * D, h, T, D, cfg->eps, s),
@@ -299,7 +302,7 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   LAUNCH(mark(7), "event record");
   {
     GemmArgs g = gemm_args(h, w->w_up, T, F, D);
-    g.out = u;
+    g.out = q && lean ? nullptr : u;
     g.out_codes = qb;  // MXFP8: u also as codes for the down linear
     g.out_scales = qbs;
     LAUNCH(linear(q ? EPI_GELU_MX : EPI_GELU, g, q ? q->w_up : nullptr,
@@ -448,7 +451,8 @@ int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_
   for (int l = 0; l < st->n_blocks; ++l) {
     const int rc = forward_impl(&bc, cur, cond, &w->blocks[l], positions, nxt, at<void>(ws, p.block),
                                 p.block_bytes, stream, nullptr, 0,
-                                mods ? mods + (size_t)l * 6 * D : nullptr, q ? &q[l] : nullptr);
+                                mods ? mods + (size_t)l * 6 * D : nullptr, q ? &q[l] : nullptr,
+                                /*lean=*/q != nullptr);
     if (rc != H3DIT_OK) return rc;
     float *t = cur;
     cur = nxt;

@@ -21,10 +21,13 @@ hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *s
                                    const double *scale, void *h, int T, int D, float eps,
                                    hipStream_t s);
 
-// same, and the bf16 output also as MXFP8 codes [T, D] + scales (D % 128 == 0)
+// same, and the bf16 output also as MXFP8 codes [T, D] + scales (D % 128 == 0);
+// with keep_h false h may not be written (it is still needed as scratch for
+// rows longer than 8192)
 hipError_t launch_rmsnorm_modulate_mx(const void *x, bool x_is_f32, const double *shift,
                                       const double *scale, void *h, uint8_t *codes,
-                                      uint8_t *scales, int T, int D, float eps, hipStream_t s);
+                                      uint8_t *scales, int T, int D, float eps, hipStream_t s,
+                                      bool keep_h = true);
 
 // same, fp32 output (the final layer of the DiT stack)
 hipError_t launch_rmsnorm_modulate_f32out(const void *x, bool x_is_f32, const double *shift,
@@ -89,7 +92,8 @@ hipError_t launch_mxfp8_quantize(const void *x, int rows, int K, uint8_t *codes,
 // o[T, A] = attention over qk [T, 2A] and vt [H, 128, Tp]
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
                             hipStream_t s);
-// The same, o also as MXFP8 codes [T, H * 128] and scales (mxfp8_quantize layout).
+// The same, o also as MXFP8 codes [T, H * 128] and scales (mxfp8_quantize layout);
+// o may be null (then only the codes and scales are written).
 hipError_t launch_attention_mx(const void *qk, const void *vt, void *o, uint8_t *o_codes,
                                uint8_t *o_scales, int T, int H, int Tp, hipStream_t s);
 

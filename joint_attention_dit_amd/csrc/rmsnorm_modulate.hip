@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(
         double o[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[j] = (double)Chunk8<XT>::at(v[k][i], j) * rs[k] * sc1[j] + sh[j];
-        store8<OT>(h + (int64_t)row * D + c * 8, o);
+        if (!MX || h) store8<OT>(h + (int64_t)row * D + c * 8, o);  // MX: h may be left out
         if constexpr (MX) {
           // chunks 4m .. 4m + 3 (lanes 4m' .. 4m' + 3; D % 128 == 0, so a group
           // of four lanes is active or idle together) form one block of 32
@@ -238,7 +238,8 @@ hipError_t launch_rmsnorm_modulate(const void *x, bool x_is_f32, const double *s
 
 hipError_t launch_rmsnorm_modulate_mx(const void *x, bool x_is_f32, const double *shift,
                                       const double *scale, void *h, uint8_t *codes,
-                                      uint8_t *scales, int T, int D, float eps, hipStream_t s) {
+                                      uint8_t *scales, int T, int D, float eps, hipStream_t s,
+                                      bool keep_h) {
   const int per_lane = (int)ceil_div(D, 64 * 8);
   if (D % 128 != 0) return hipErrorInvalidValue;
   if (per_lane > 16) {  // long rows: the two-pass normalisation, then the quantisation
@@ -246,6 +247,7 @@ hipError_t launch_rmsnorm_modulate_mx(const void *x, bool x_is_f32, const double
     if (e != hipSuccess) return e;
     return launch_mxfp8_quantize(h, T, D, codes, scales, s);
   }
+  if (!keep_h) h = nullptr;  // only the codes and scales are written
   const int blocks = (int)ceil_div(T, x_is_f32 ? 4 : 8);  // 4 waves of 1 (fp32) or 2 rows
   auto reg = [&](auto nc_c) {
     constexpr int NC = decltype(nc_c)::value;
