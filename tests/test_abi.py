@@ -126,6 +126,16 @@ def test_stage_validation(lib):
                                None) == B.H3DIT_EUNSUPPORTED
     assert lib.h3dit_out_proj_residual(ctypes.byref(cfg), P["x"], P["w_o"], P["x"], 3, P["mod"],
                                        P["out"], None) == B.H3DIT_EINVAL
+    # the MXFP8 attention entry: null codes / scales, unsupported head size,
+    # misaligned codes (all rejected on the host, before any HIP call)
+    assert lib.h3dit_attention_mxfp8(ctypes.byref(cfg), P["x"], P["x"], P["h"], None, P["mod"],
+                                     None) == B.H3DIT_EINVAL
+    assert lib.h3dit_attention_mxfp8(ctypes.byref(cfg), P["x"], P["x"], P["h"], P["out"], None,
+                                     None) == B.H3DIT_EINVAL
+    assert lib.h3dit_attention_mxfp8(ctypes.byref(full_cfg(head_dim=96)), P["x"], P["x"], P["h"],
+                                     P["out"], P["mod"], None) == B.H3DIT_EUNSUPPORTED
+    assert lib.h3dit_attention_mxfp8(ctypes.byref(cfg), P["x"], P["x"], P["h"], P["out"] + 4,
+                                     P["mod"], None) == B.H3DIT_EALIGN
 
 
 def test_fault_injection_reports_hip_error(lib, monkeypatch):
