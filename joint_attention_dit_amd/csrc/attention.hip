@@ -284,12 +284,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
         for (int qb = 0; qb < 2; ++qb)
           oacc[db][qb] = mfma16(vf, __builtin_bit_cast(bf16x8, pf[ks][qb]), oacc[db][qb]);
       }
-    // fragment reads run four reads (eight MFMAs) ahead of their use
+    // fragment reads run four reads (eight MFMAs) ahead of their use, two
+    // reads after every four products
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int k = 0; k < 12; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int k = 0; k < 6; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };

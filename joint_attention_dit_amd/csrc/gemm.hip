@@ -173,9 +173,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
           fb[BCUR ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + j * 16 * BK);
       }
       fa[i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + i * 16 * BK);
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      if (i == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      // the next k-step's B fragments two reads per two products, then one A
+      // fragment read per four products (measured: the fastest of the
+      // groupings tried)
+      if (i == 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
   };
   using I0 = std::integral_constant<int, 0>;
