@@ -98,7 +98,10 @@ int h3dit_workspace_size(const h3dit_config *cfg, size_t *bytes);
  *   x          [T, D], dtype cfg->x_dtype (bf16 or fp32)
  *   cond       [D] fp32 conditioning vector (the timestep embedding)
  *   w          weights (see h3dit_weights)
- *   positions  [T, 2] int32 RoPE positions (row, col); any int32 values
+ *   positions  [T, 2] int32 RoPE positions (row, col); every int32 value is
+ *              accepted (each becomes an fp64 angle; no range makes the
+ *              kernels fail), so positions are not range-checked: a check
+ *              would need a device-to-host copy and a synchronisation
  *   out        [T, D] fp32; must not overlap x or the workspace
  *   workspace  >= h3dit_workspace_size() bytes; contents are scratch
  */
@@ -153,19 +156,24 @@ int h3dit_modulation(const h3dit_config *cfg, const void *w_ada, const float *co
 int h3dit_modulation_table(const h3dit_config *cfg, const void *w_ada, const float *conds,
                            int n, double *mods, void *stream);
 
-/* Steps 2 and 7, RMSNorm + modulation (spec page, "RMS Normalization"):
+/* Steps 2 and 7, RMSNorm + modulation (spec page, "Specifications": RMS
+ * Normalization; "Architecture Diagram": "AdaLN Modulation", scale and shift):
  * h[T, D] bf16 = bf16( x / sqrt(mean(x^2) + eps) * (1 + scale) + shift ),
  * computed in fp64; x is [T, D] of dtype x_dtype; shift, scale are fp64 [D]. */
 int h3dit_rmsnorm_modulate(const h3dit_config *cfg, const void *x, int32_t x_dtype,
                            const double *shift, const double *scale, void *h, void *stream);
 
-/* RoPE table for step 4 (model card: multimodal RoPE; 2D axial reading):
+/* RoPE table for step 4 (model card, "Model Architecture": multimodal RoPE, read
+ * as 2D axial; spec page, "Architecture Diagram": "Pos: RoPE"):
  * table[T, 64, 2] fp32: (cos, sin) of positions[t][j / 32] * rope_base^(-(j % 32)/32),
  * evaluated in fp64. */
 int h3dit_rope_table(const h3dit_config *cfg, const int32_t *positions, float *table,
                      void *stream);
 
-/* Steps 3 + 4, QKV projection with RoPE in the epilogue:
+/* Steps 3 + 4, QKV projection with RoPE in the epilogue (spec page, "Architecture
+ * Diagram": the attention block's Q, K, V projections and "Pos: RoPE"; model card,
+ * "Model Architecture": 56 query and 56 key-value heads of 128, multimodal RoPE,
+ * read as 2D axial):
  *   h [T, D] bf16, w_qkv [3A, D] bf16, table from h3dit_rope_table.
  *   qk [T, 2A] bf16: columns 0..A-1 = bf16(rope(q) * log2(e)/sqrt(128)),
  *      columns A..2A-1 = bf16(rope(k)); q and k are the fp32 products, rounded
@@ -179,25 +187,33 @@ int h3dit_rope_table(const h3dit_config *cfg, const int32_t *positions, float *t
 int h3dit_qkv_rope(const h3dit_config *cfg, const void *h, const void *w_qkv, const float *table,
                    void *qk, void *vt, void *stream);
 
-/* Step 5, joint bidirectional attention over all T tokens (no mask):
+/* Step 5, joint bidirectional attention over all T tokens, no mask (model card,
+ * "Model Architecture": text and image tokens in one packed sequence of a
+ * single-stream transformer; spec page, "Architecture Diagram": "Joint /
+ * Cross-Attention"):
  *   qk, vt as written by h3dit_qkv_rope (q pre-scaled, so softmax(q.k) in base 2);
  *   o [T, A] bf16 (head h = columns h*128..). */
 int h3dit_attention(const h3dit_config *cfg, const void *qk, const void *vt, void *o,
                     void *stream);
 
-/* Step 6, output projection + gated residual:
+/* Step 6, output projection + gated residual (spec page, "Architecture Diagram":
+ * the attention branch's output projection scaled by gate1 of the AdaLN
+ * modulation and added to the residual stream, "+"):
  *   x1[T, D] fp32 = resid + gate * (o[T, A] . w_o[D, A]^T); resid is [T, D] of
  *   dtype resid_dtype; gate fp64 [D]. */
 int h3dit_out_proj_residual(const h3dit_config *cfg, const void *o, const void *w_o,
                             const void *resid, int32_t resid_dtype, const double *gate,
                             float *x1, void *stream);
 
-/* Step 8, MLP up-projection + tanh-GELU:
+/* Step 8, MLP up-projection + tanh-GELU (spec page, "Architecture Diagram":
+ * "Feed-Forward (MLP) GELU Intermediate: 14.3k"; model card, "Model
+ * Architecture": FFN width 14336):
  *   u[T, F] bf16 = bf16(gelu_tanh(h2[T, D] . w_up[F, D]^T)). */
 int h3dit_mlp_up_gelu(const h3dit_config *cfg, const void *h2, const void *w_up, void *u,
                       void *stream);
 
-/* Step 9, MLP down-projection + gated residual:
+/* Step 9, MLP down-projection + gated residual (spec page, "Architecture
+ * Diagram": the MLP branch scaled by gate2 and added to the residual stream, "+"):
  *   out[T, D] fp32 = x1 + gate * (u[T, F] . w_down[D, F]^T); x1 fp32, gate fp64 [D]. */
 int h3dit_mlp_down_residual(const h3dit_config *cfg, const void *u, const void *w_down,
                             const float *x1, const double *gate, float *out, void *stream);

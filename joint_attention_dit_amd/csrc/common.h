@@ -54,8 +54,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // completion themselves (s_waitcnt vmcnt before the barrier that publishes
 // the tile).
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-               "s"(base), "s"(lds_addr)
+  // m0 (the LDS destination) is an input constraint, so the compiler knows the
+  // block reads it; the s_nop covers the m0 -> LDS-DMA hazard
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "{m0}"(lds_addr)
                : "memory");
 }
 

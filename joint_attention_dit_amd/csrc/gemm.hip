@@ -272,7 +272,7 @@ static hipError_t launch_epi(const GemmArgs &a0, hipStream_t s) {
   GemmArgs a = a0;
   const int tiles = (int)(ceil_div(a.N, BN) * ceil_div(a.M, BT));
   int rem = 0;
-  a.split = a.partial ? plan_split(a.M, a.N, a.K / BK, device_cus(), a.partial_bytes, &rem) : 1;
+  a.split = a.partial ? plan_split(a.M, a.N, a.K / BK, kPlanCus, a.partial_bytes, &rem) : 1;
   a.full_tiles = tiles - (a.split > 1 ? rem : 0);
   const int grid = a.split > 1 ? a.full_tiles + rem * a.split : tiles;
   hipLaunchKernelGGL(gemm_kernel<EPI>, dim3(grid), dim3(512), 0, s, a);

@@ -287,20 +287,10 @@ __global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
     }
 }
 
-// Compute units of the current device (cached per device).
-constexpr int kPlanCus = 256;  // MI355X; scratch is sized for it, larger devices split less
-static int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
+// The split plan is made for MI355X's 256 compute units on every device, so
+// the order in which a tile's K slices are summed (and with it the fp32
+// rounding of the result) never depends on the device the library runs on.
+constexpr int kPlanCus = 256;
 
 // One workgroup per CU at a time. The last, partial wave of `rem` tiles is cut
 // along K into s slices (a second kernel adds them) when that shortens it: cut

@@ -61,12 +61,11 @@ __device__ __forceinline__ void dma16_lanes8(const void *base, uint32_t voff, ui
   asm volatile(
       "s_mov_b64 %0, exec\n\t"
       "s_mov_b64 exec, 0xff\n\t"
-      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b64 exec, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(base), "s"(lds_addr)
+      : "v"(voff), "s"(base), "{m0}"(lds_addr)
       : "memory");
 }
 
@@ -325,7 +324,7 @@ static hipError_t launch_mx_epi(const GemmArgs &a0, hipStream_t s) {
   GemmArgs a = a0;
   const int tiles = (int)(ceil_div(a.N, BN) * ceil_div(a.M, BT));
   int rem = 0;
-  a.split = a.partial ? plan_split(a.M, a.N, a.K / KT, device_cus(), a.partial_bytes, &rem) : 1;
+  a.split = a.partial ? plan_split(a.M, a.N, a.K / KT, kPlanCus, a.partial_bytes, &rem) : 1;
   a.full_tiles = tiles - (a.split > 1 ? rem : 0);
   const int grid = a.split > 1 ? a.full_tiles + rem * a.split : tiles;
   hipLaunchKernelGGL(gemm_mx_kernel<EPI>, dim3(grid), dim3(512), 0, s, a);

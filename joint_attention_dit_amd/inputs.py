@@ -86,6 +86,19 @@ CONFIGS: Dict[str, BlockConfig] = {
         x_dtype="bf16",
         description="edit-shaped block: 2048x2048 target + 4 references of 64x64 + 1024 text = 21504 tokens",
         **_FULL),
+    # one GPU's token share of the 4096x4096 block under G-way Ulysses sequence
+    # parallelism (vLLM blog, "Inference Optimizations", and the serving
+    # recipe's deployment profiles: SP4 is the default layout): T / G tokens
+    # through the per-token kernels, laid out as 512 / G text tokens and
+    # 128-column image rows of the canvas
+    "share4": BlockConfig(
+        "share4", text_tokens=128, images=((32, 128, 0),), x_dtype="bf16",
+        description="4-way Ulysses share of the 4096x4096 block: 128 text + 32x128 image = 4224 tokens",
+        **_FULL),
+    "share8": BlockConfig(
+        "share8", text_tokens=64, images=((16, 128, 0),), x_dtype="bf16",
+        description="8-way Ulysses share of the 4096x4096 block: 64 text + 16x128 image = 2112 tokens",
+        **_FULL),
     # non-square canvas (2720x1536 -> 85x48 tokens): ragged tiles everywhere
     "nonsquare": BlockConfig(
         "nonsquare", text_tokens=256, images=((48, 85, 0),), x_dtype="bf16",

@@ -1,10 +1,11 @@
-"""Writes tests/golden/tiny_block_exact.json from the float64 oracle.
+"""Writes tests/golden/tiny_block_exact.json and tiny_block_contract.json from
+the float64 oracle.
 
-The pages print no worked numeric example for the block, so this fixture is
-not a page value: it is a regression record of the oracle itself (exact mode,
-tiny block, seed 0), written only by this script, which calls nothing but the
-oracle and the seeded input generators. Re-run it only when a change to the
-oracle's arithmetic is justified by a reading of the pages.
+The pages print no worked numeric example for the block, so these fixtures are
+not page values: they are regression records of the oracle itself (exact mode
+and contract mode, tiny block, seed 0), written only by this script, which
+calls nothing but the oracle and the seeded input generators. Re-run it only
+when a change to the oracle's arithmetic is justified by a reading of the pages.
 """
 import json
 import os
@@ -20,20 +21,26 @@ ROWS = [0, 1, 31, 32, 33, 100, 200, 287]
 COLS = [0, 1, 2, 63, 64, 127, 128, 255]
 
 
-def compute():
+def compute(mode: str = "exact"):
     cfg = CONFIGS["tiny"]
     inp = make_inputs(cfg, seed=0)
     w = {k: to_numpy_f64(inp[k]) for k in ("w_ada", "w_qkv", "w_o", "w_up", "w_down")}
     r = O.block_forward(to_numpy_f64(inp["x"]), to_numpy_f64(inp["cond"]), w,
-                        inp["positions"].numpy(), heads=cfg.heads, mode="exact")
-    return {
-        "config": "tiny", "seed": 0, "mode": "exact", "rows": ROWS, "cols": COLS,
+                        inp["positions"].numpy(), heads=cfg.heads, mode=mode)
+    rec = {
+        "config": "tiny", "seed": 0, "mode": mode, "rows": ROWS, "cols": COLS,
         "out": [[r["out"][i, j] for j in COLS] for i in ROWS],
         "x1": [[r["x1"][i, j] for j in COLS] for i in ROWS],
         "mod_first8": list(r["mod"][:8]),
     }
+    if mode == "contract":  # the bf16 intermediates at the same rows and columns
+        for key in ("h1", "o", "h2"):
+            rec[key] = [[r[key][i, j] for j in COLS] for i in ROWS]
+        rec["u"] = [[r["u"][i, j] for j in COLS + [511, 1023]] for i in ROWS]
+    return rec
 
 
 if __name__ == "__main__":
-    with open(os.path.join(HERE, "tiny_block_exact.json"), "w") as f:
-        json.dump(compute(), f, indent=1)
+    for mode in ("exact", "contract"):
+        with open(os.path.join(HERE, f"tiny_block_{mode}.json"), "w") as f:
+            json.dump(compute(mode), f, indent=1)
