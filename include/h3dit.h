@@ -109,6 +109,25 @@ int h3dit_block_forward(const h3dit_config *cfg, const void *x, const float *con
                         const h3dit_weights *w, const int32_t *positions, float *out,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* Bytes of the library's static device scratch used by h3dit_block_forward_noalloc. */
+#define H3DIT_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* h3dit_block_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same result, bitwise, with the
+ * workspace taken from a static device array of H3DIT_NOALLOC_SCRATCH_BYTES
+ * (256 MiB) that each GPU the library runs on holds until the process ends.
+ * The call allocates nothing. Shapes whose h3dit_workspace_size() exceeds
+ * that size return H3DIT_EWORKSPACE before any HIP call (at full width,
+ * hidden 5376, that is above about 1,500 tokens). The array belongs to the
+ * current device (hipSetDevice), which must be the device of `stream`; calls
+ * on one GPU share it, so two calls that overlap in time on the same GPU (on
+ * different streams, or from different threads) race: order them on one
+ * stream. Nothing in the array needs to start at zero. */
+int h3dit_block_forward_noalloc(const h3dit_config *cfg, const void *x, const float *cond,
+                                const h3dit_weights *w, const int32_t *positions, float *out,
+                                void *stream);
+
 /* Same as h3dit_block_forward, and records caller-created hipEvent_t handles
  * between the stages: events[i] is recorded on `stream` before stage i and
  * events[9] after the last, for stages (0) modulation, (1) RoPE table,

@@ -32,7 +32,9 @@ EXPORTED = (
     "h3dit_linear_mxfp8", "h3dit_workspace_size_mxfp8", "h3dit_block_forward_mxfp8",
     "h3dit_block_forward_mxfp8_timed", "h3dit_workspace_layout", "h3dit_stack_workspace_size_mxfp8",
     "h3dit_dit_forward_mxfp8", "h3dit_dit_forward_mod_mxfp8", "h3dit_attention_mxfp8",
+    "h3dit_block_forward_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 256 << 20   # H3DIT_NOALLOC_SCRATCH_BYTES
 
 
 class H3ditError(RuntimeError):
@@ -93,6 +95,7 @@ def load_library() -> ctypes.CDLL:
     sigs = {
         "h3dit_workspace_size": [cfgp, ctypes.POINTER(sz)],
         "h3dit_block_forward": [cfgp, vp, vp, ctypes.POINTER(Weights), vp, vp, vp, sz, vp],
+        "h3dit_block_forward_noalloc": [cfgp, vp, vp, ctypes.POINTER(Weights), vp, vp, vp],
         "h3dit_block_forward_timed": [cfgp, vp, vp, ctypes.POINTER(Weights), vp, vp, vp, sz, vp,
                                       ctypes.POINTER(vp), ctypes.c_int],
         "h3dit_modulation": [cfgp, vp, vp, vp, vp],
@@ -213,6 +216,15 @@ def h3dit_block_forward(cfg: Config, x: torch.Tensor, cond: torch.Tensor,
         ctypes.byref(cfg), _ptr(x), _ptr(cond), ctypes.byref(ws), _ptr(positions), _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
         "h3dit_block_forward")
+
+
+def h3dit_block_forward_noalloc(cfg: Config, x: torch.Tensor, cond: torch.Tensor,
+                                w: Dict[str, torch.Tensor], positions: torch.Tensor,
+                                out: torch.Tensor, stream=None) -> None:
+    ws = weights_struct(w)
+    _check(load_library().h3dit_block_forward_noalloc(
+        ctypes.byref(cfg), _ptr(x), _ptr(cond), ctypes.byref(ws), _ptr(positions), _ptr(out),
+        _stream(stream)), "h3dit_block_forward_noalloc")
 
 
 def h3dit_block_forward_timed(cfg: Config, x, cond, w, positions, out, workspace,

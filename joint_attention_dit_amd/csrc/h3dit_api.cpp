@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/h3dit.h"
 #include "kernels.h"
@@ -472,9 +473,65 @@ int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_
   return ok();
 }
 
+// ---- the block forward without a workspace argument ----------------------
+// Its scratch is this file-scope device array; each GPU holds its own copy at
+// its own address. In host code `scratch` names a host-side stand-in, so the
+// device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever handed to kernels.
+__device__ __align__(256) unsigned char scratch[H3DIT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+int scratch_address(void **ptr) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(H3DIT_EUNSUPPORTED, "device %d: at most %d devices are supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    const hipError_t e2 = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e2 != hipSuccess) return hip_fail(e2, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(H3DIT_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return H3DIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int h3dit_block_forward_noalloc(const h3dit_config *cfg, const void *x, const float *cond,
+                                const h3dit_weights *w, const int32_t *positions, float *out,
+                                void *stream) {
+  // every argument check before the first HIP call (forward_impl repeats them)
+  CHECK_CFG(cfg);
+  if (!w) return fail(H3DIT_EINVAL, "w is NULL");
+  CHECK_PTR(x);
+  CHECK_PTR(cond);
+  CHECK_PTR(positions);
+  CHECK_PTR(out);
+  CHECK_PTR(w->w_ada);
+  CHECK_PTR(w->w_qkv);
+  CHECK_PTR(w->w_o);
+  CHECK_PTR(w->w_up);
+  CHECK_PTR(w->w_down);
+  const size_t need = make_plan(cfg).total;
+  if (need > (size_t)H3DIT_NOALLOC_SCRATCH_BYTES)
+    return fail(H3DIT_EWORKSPACE, "this block needs %zu bytes of scratch; the static scratch "
+                "holds %zu (use h3dit_block_forward with a workspace)", need,
+                (size_t)H3DIT_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != H3DIT_OK) return st;
+  return forward_impl(cfg, x, cond, w, positions, out, ws, need, stream, nullptr, 0);
+}
 
 int h3dit_stack_workspace_size(const h3dit_config *cfg, const h3dit_stack_config *st,
                                size_t *bytes) {
