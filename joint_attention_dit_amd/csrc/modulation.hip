@@ -7,6 +7,9 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+#include <type_traits>
+
 namespace h3dit {
 
 __global__ __launch_bounds__(256) void modulation_kernel(const bf16 *__restrict__ w,
@@ -31,6 +34,55 @@ __global__ __launch_bounds__(256) void modulation_kernel(const bf16 *__restrict_
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (lane == 0) mod[row] = acc;
+}
+
+// The same GEMV as a persistent kernel for rows of up to 8192 columns: one
+// workgroup of 16 waves per CU stages cond in LDS once (every row reads all of
+// it: twice the row's own bytes), then each wave takes rows w, w + W, ... (w
+// numbered wave-major across the workgroups, W waves in all), issuing all of a
+// row's 16-byte weight loads at once. Each lane accumulates the same products
+// in the same order as modulation_kernel (its chunks ascending, the eight
+// elements of a chunk in turn) and the same shuffle tree sums the lanes, so
+// the result is bitwise that of the one-row-per-wave kernel. LDS layout: half
+// hh (elements 4 hh .. 4 hh + 3) of chunk c at float4 index hh * 64 NC + c.
+template <int NC>
+__global__ __launch_bounds__(1024) void modulation_lds_kernel(const bf16 *__restrict__ w,
+                                                             const float *__restrict__ cond,
+                                                             double *__restrict__ mod, int rows,
+                                                             int cols) {
+  constexpr int PL = 64 * NC;
+  extern __shared__ f32x4 cond_lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunks = cols >> 3;
+  for (int i = tid; i < 2 * chunks; i += 1024)
+    cond_lds[(i & 1) * PL + (i >> 1)] = reinterpret_cast<const f32x4 *>(cond)[i];
+  __syncthreads();
+  const int W = (int)gridDim.x * 16;
+  for (int row = wave * (int)gridDim.x + (int)blockIdx.x; row < rows; row += W) {
+    const bf16 *wr = w + (int64_t)row * cols;
+    bf16x8 wv[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) wv[i] = *reinterpret_cast<const bf16x8 *>(wr + c * 8);
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) {
+        const f32x4 c0 = cond_lds[c], c1 = cond_lds[PL + c];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc += (double)(float)wv[i][j] * (double)c0[j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc += (double)(float)wv[i][4 + j] * (double)c1[j];
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) mod[row] = acc;
+  }
 }
 
 // The same products for up to MAXS conditioning vectors per pass over the
@@ -89,6 +141,19 @@ hipError_t launch_modulation_multi(const void *w, const float *conds, int n, dou
 
 hipError_t launch_modulation(const void *w, const float *cond, double *mod, int rows, int cols,
                              hipStream_t s) {
+  const int per_lane = (int)ceil_div(cols, 64 * 8);  // 16-byte weight chunks per lane
+  auto lds = [&](auto nc_c) {
+    constexpr int NC = decltype(nc_c)::value;
+    const int grid = (int)std::min<int64_t>(256, ceil_div(rows, 16));
+    hipLaunchKernelGGL(modulation_lds_kernel<NC>, dim3(grid), dim3(1024),
+                       (size_t)2 * 64 * NC * sizeof(f32x4), s, static_cast<const bf16 *>(w), cond,
+                       mod, rows, cols);
+    return hipGetLastError();
+  };
+  if (per_lane <= 4) return lds(std::integral_constant<int, 4>());
+  if (per_lane <= 8) return lds(std::integral_constant<int, 8>());
+  if (per_lane <= 11) return lds(std::integral_constant<int, 11>());
+  if (per_lane <= 16) return lds(std::integral_constant<int, 16>());
   const int blocks = (int)ceil_div(rows, 4);
   hipLaunchKernelGGL(modulation_kernel, dim3(blocks), dim3(256), 0, s,
                      static_cast<const bf16 *>(w), cond, mod, rows, cols);

@@ -13,6 +13,7 @@
 #include "kernels.h"
 #include "mxfp8_device.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace h3dit {
@@ -162,6 +163,119 @@ __global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(
   }
 }
 
+// Persistent form for rows of up to 8192 elements: one workgroup per CU stages
+// (1 + scale) and shift (fp64) in LDS once, then each wave normalises rows
+// w, w + W, ... (W waves in all; w numbers the waves wave-major across the
+// workgroups, so the waves with one row more than the others are spread over
+// all CUs), one row at a time, held in registers between the two passes.
+// The per-row fp64 modulation vectors then come from LDS rather than from L2
+// (for bf16 rows they are 16x the row's own bytes), and the many waves per CU
+// (16 for bf16 rows, 12 for fp32 rows) keep enough row loads in flight.
+// LDS layout: element 8 c + 2 q + e of array a (0: 1 + scale, 1: shift) at
+// double index ((a * 4 + q) * 64 NC + c) * 2 + e (NC: chunks per lane), so the
+// 16-byte reads of consecutive lanes (consecutive c) are consecutive and every
+// read of a lane is an immediate offset from one of two base addresses.
+// Threads per workgroup: as many waves as the registers allow (fp32 rows, the
+// MXFP8 epilogue and the longest rows take more registers per wave).
+template <typename XT, int NC, bool MX>
+struct LdsNorm {
+  static constexpr int waves = (sizeof(XT) == 2 ? 16 : 12) - (MX || NC > 11 ? 4 : 0);
+  static constexpr int threads = 64 * waves;
+};
+
+// Keeps v opaque to the compiler between the two passes, so it re-converts
+// the stored elements instead of holding 8 doubles per chunk across them.
+__device__ __forceinline__ void opaque(bf16x8 &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(Chunk8<float>::raw &v) {
+  asm volatile("" : "+v"(v.a), "+v"(v.b));
+}
+
+template <typename XT, int NC, typename OT, bool MX = false>
+__global__ __launch_bounds__((LdsNorm<XT, NC, MX>::threads)) void rmsnorm_modulate_lds_kernel(
+    const XT *__restrict__ x, const double *__restrict__ shift, const double *__restrict__ scale,
+    OT *__restrict__ h, int T, int D, double eps, uint8_t *__restrict__ codes = nullptr,
+    uint8_t *__restrict__ scales = nullptr) {
+  constexpr int NT = LdsNorm<XT, NC, MX>::threads, NWG = NT / 64;
+  extern __shared__ __attribute__((aligned(16))) double mod_lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunks = D >> 3;
+  constexpr int PL = NC * 64;  // chunks per plane (a compile-time stride: immediate offsets)
+  for (int i = tid; i < D; i += NT) {
+    const int c = i >> 3, q = (i >> 1) & 3, e = i & 1;
+    mod_lds[((0 * 4 + q) * PL + c) * 2 + e] = 1.0 + scale[i];
+    mod_lds[((1 * 4 + q) * PL + c) * 2 + e] = shift[i];
+  }
+  __syncthreads();
+  const int W = (int)gridDim.x * NWG;
+  for (int row = wave * (int)gridDim.x + (int)blockIdx.x; row < T; row += W) {
+    typename Chunk8<XT>::raw v[NC];
+    const XT *xr = x + (int64_t)row * D;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) v[i] = Chunk8<XT>::fetch(xr + c * 8);
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      if (lane + 64 * i < chunks) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double e = (double)Chunk8<XT>::at(v[i], j);
+          ss += e * e;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const double rs = 1.0 / sqrt(ss / (double)D + eps);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) opaque(v[i]);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) {
+        double sc1[8], sh[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f64x2 a = *reinterpret_cast<const f64x2 *>(mod_lds + ((0 * 4 + q) * PL + c) * 2);
+          const f64x2 b = *reinterpret_cast<const f64x2 *>(mod_lds + ((1 * 4 + q) * PL + c) * 2);
+          sc1[2 * q] = a[0];
+          sc1[2 * q + 1] = a[1];
+          sh[2 * q] = b[0];
+          sh[2 * q + 1] = b[1];
+        }
+        double o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = (double)Chunk8<XT>::at(v[i], j) * rs * sc1[j] + sh[j];
+        if (!MX || h) store8<OT>(h + (int64_t)row * D + c * 8, o);  // MX: h may be left out
+        if constexpr (MX) {
+          float g[8];
+          uint32_t amax = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const bf16 bv = to_bf16(o[j]);
+            g[j] = (float)bv;
+            amax = max(amax, (uint32_t)__builtin_bit_cast(uint16_t, bv) & 0x7FFFu);
+          }
+          amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+          amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+          const int sbyte = mx_scale_byte(amax);
+          const float inv = mx_inv_scale(sbyte);
+          const u32x2 qv = {mx_code4(g[0], g[1], g[2], g[3], inv),
+                            mx_code4(g[4], g[5], g[6], g[7], inv)};
+          *reinterpret_cast<u32x2 *>(codes + (int64_t)row * D + c * 8) = qv;
+          if ((lane & 3) == 0) scales[mx_scale_offset(row, c >> 2, D)] = (uint8_t)sbyte;
+        }
+      }
+      // one chunk at a time: the other waves of the CU hide the LDS latency,
+      // and the chunks' fp64 temporaries never pile up in registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Longer rows: two passes over memory.
 template <typename XT, typename OT>
 __global__ __launch_bounds__(256) void rmsnorm_modulate_kernel(const XT *__restrict__ x,
@@ -200,9 +314,49 @@ __global__ __launch_bounds__(256) void rmsnorm_modulate_kernel(const XT *__restr
   }
 }
 
+// One workgroup per CU (its LDS holds 16 D bytes); fewer when there are fewer
+// rows than waves.
+static int lds_grid(int T, int waves) { return (int)std::min<int64_t>(256, ceil_div(T, waves)); }
+
+template <typename OT, bool MX>
+static hipError_t launch_rn_lds(const void *x, bool x_is_f32, const double *shift,
+                                const double *scale, OT *h, int T, int D, float eps, hipStream_t s,
+                                uint8_t *codes, uint8_t *scales) {
+  auto go = [&](auto nc_c) {
+    constexpr int NC = decltype(nc_c)::value;
+    const size_t lds = (size_t)16 * 64 * 8 * NC;  // 2 arrays x 4 planes x 64 NC x 16 bytes
+    if (x_is_f32) {
+      auto k = rmsnorm_modulate_lds_kernel<float, NC, OT, MX>;
+      hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds);
+      if (e != hipSuccess) return e;
+      constexpr int nt = LdsNorm<float, NC, MX>::threads;
+      hipLaunchKernelGGL(k, dim3(lds_grid(T, nt / 64)), dim3(nt), lds, s, static_cast<const float *>(x),
+                         shift, scale, h, T, D, (double)eps, codes, scales);
+    } else {
+      auto k = rmsnorm_modulate_lds_kernel<bf16, NC, OT, MX>;
+      hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds);
+      if (e != hipSuccess) return e;
+      constexpr int nt = LdsNorm<bf16, NC, MX>::threads;
+      hipLaunchKernelGGL(k, dim3(lds_grid(T, nt / 64)), dim3(nt), lds, s, static_cast<const bf16 *>(x),
+                         shift, scale, h, T, D, (double)eps, codes, scales);
+    }
+    return hipGetLastError();
+  };
+  const int per_lane = (int)ceil_div(D, 64 * 8);  // 16-byte chunks per lane
+  if (per_lane <= 1) return go(std::integral_constant<int, 1>());
+  if (per_lane <= 4) return go(std::integral_constant<int, 4>());
+  if (per_lane <= 8) return go(std::integral_constant<int, 8>());
+  if (per_lane <= 11) return go(std::integral_constant<int, 11>());
+  return go(std::integral_constant<int, 16>());
+}
+
 template <typename OT>
 static hipError_t launch_rn(const void *x, bool x_is_f32, const double *shift, const double *scale,
                             OT *h, int T, int D, float eps, hipStream_t s) {
+  if (D <= 8192)
+    return launch_rn_lds<OT, false>(x, x_is_f32, shift, scale, h, T, D, eps, s, nullptr, nullptr);
   const int blocks = (int)ceil_div(T, 4);
   const int reg_blocks = (int)ceil_div(T, x_is_f32 ? 4 : 8);  // 4 waves of 1 (fp32) or 2 rows
   auto reg = [&](auto nc_c) {
@@ -248,6 +402,9 @@ hipError_t launch_rmsnorm_modulate_mx(const void *x, bool x_is_f32, const double
     return launch_mxfp8_quantize(h, T, D, codes, scales, s);
   }
   if (!keep_h) h = nullptr;  // only the codes and scales are written
+  if (D <= 8192)
+    return launch_rn_lds<bf16, true>(x, x_is_f32, shift, scale, static_cast<bf16 *>(h), T, D, eps,
+                                     s, codes, scales);
   const int blocks = (int)ceil_div(T, x_is_f32 ? 4 : 8);  // 4 waves of 1 (fp32) or 2 rows
   auto reg = [&](auto nc_c) {
     constexpr int NC = decltype(nc_c)::value;
