@@ -65,6 +65,9 @@ constexpr int KT = 64;             // keys per tile
 constexpr int K_ELEMS = KT * 128;  // bf16 elements of one K tile (16 KB)
 constexpr int V_ELEMS = 128 * KT;  // bf16 elements of one V^T tile (16 KB)
 constexpr int VSTAGE0 = 2 * K_ELEMS;  // [K0 | K1 | V0 | V1], 64 KB
+// one key-range piece of an item: O^T-unnormalised [256 queries][128 dims],
+// the weight sums [256] and the shifts [256], fp32
+constexpr int PIECE_FLOATS = QT * 130;
 // The first shift lies SHIFT_BIAS above the first tile's maximum, and a
 // lane's weight sum per query and tile above SUM_LIMIT forces the second pass:
 // a score more than about 104 (base 2) above the first tile's maximum. The
@@ -92,7 +95,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
                                                                 bf16 *__restrict__ o,
                                                                 uint8_t *__restrict__ o_codes,
                                                                 uint8_t *__restrict__ o_scales,
-                                                                int T, int H, int Tp) {
+                                                                int T, int H, int Tp,
+                                                                float *__restrict__ part,
+                                                                int full, int split) {
   __shared__ __attribute__((aligned(1024))) bf16 lds[2 * K_ELEMS + 2 * V_ELEMS];
   __shared__ int rerun;  // some wave of the workgroup needs pass 1
 
@@ -105,19 +110,35 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   // is remapped so that each XCD receives a contiguous range of (head, query
   // tile) items, head-major: the workgroups in flight on one XCD then work on
   // the same one or two heads and stream the same K and V tiles through its L2.
+  // With split > 1, workgroups full, full + 1, ... each take one key range
+  // (piece) of the items full, full + 1, ... (the last, partial round of
+  // items): piece p of an item covers key tiles [p per, min((p + 1) per, all)).
+  // Their unnormalised outputs, weight sums and shifts go to `part`, and
+  // attention_merge_kernel combines the pieces.
   const int qtiles = (int)ceil_div(T, QT);
-  int h, qt;
+  const int all_tiles = (int)ceil_div(T, KT);
+  int h, qt, L, piece = -1, kt0 = 0, kt1 = all_tiles;
   {
-    const int n = (int)gridDim.x, bid = (int)blockIdx.x;
-    const int xcd = bid & 7, idx = bid >> 3, q = n >> 3, rem = n & 7;
-    const int L = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + idx;
+    const int bid = (int)blockIdx.x;
+    if (split <= 1 || bid < full) {
+      const int n = split <= 1 ? (int)gridDim.x : full;
+      const int xcd = bid & 7, idx = bid >> 3, q = n >> 3, rem = n & 7;
+      L = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + idx;
+    } else {
+      const int u = bid - full;
+      L = full + u / split;
+      piece = u - (u / split) * split;
+      const int per = (int)ceil_div(all_tiles, split);
+      kt0 = piece * per;
+      kt1 = min(kt0 + per, all_tiles);
+    }
     h = L / qtiles;
     qt = L - h * qtiles;
   }
   const int A = H * 128;
   const int ldqk = 2 * A;
   const int q0 = qt * QT + wave * 32;
-  const int ntiles = (int)ceil_div(T, KT);
+  const int ntiles = kt1 - kt0;  // key tiles of this workgroup; `tile` below counts from kt0
 
   // this lane's query fragments: Q[q0 + 16 qb + r][32 s + 8 g .. +7], s = 0..3
   bf16x8 qf[2][4];
@@ -150,8 +171,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   }
   auto kload = [&](int stage, int tile) {
     const uint32_t dst = lds0 + (uint32_t)(stage * K_ELEMS + wave * 2 * 512) * 2u;
-    const bf16 *base = khead + (int64_t)tile * KT * ldqk;
-    const int rows = T - tile * KT;  // keys present in this tile
+    const bf16 *base = khead + (int64_t)(kt0 + tile) * KT * ldqk;
+    const int rows = T - (kt0 + tile) * KT;  // keys present in this tile
     if (rows >= KT) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) dma16(base, kofs[j], dst + j * 1024);
@@ -163,7 +184,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   };
   auto vload = [&](int stage, int tile) {
     const uint32_t dst = lds0 + (uint32_t)(VSTAGE0 + stage * V_ELEMS + wave * 2 * 512) * 2u;
-    const bf16 *base = vhead + tile * KT;
+    const bf16 *base = vhead + (kt0 + tile) * KT;
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(base, vofs[j], dst + j * 1024);
   };
@@ -208,7 +229,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
     constexpr int D = decltype(d_c)::value;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int row = min(tile * KT + 16 * b + r, T - 1);
+      const int row = min((kt0 + tile) * KT + 16 * b + r, T - 1);
       const bf16 *kp = khead + (int64_t)row * ldqk + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -223,7 +244,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
   // keys past T of tile `tile` get zero weight
   auto mask = [&](auto d_c, int tile) {
     constexpr int D = decltype(d_c)::value;
-    const int kv0 = tile * KT;
+    const int kv0 = (kt0 + tile) * KT;
     if (kv0 + KT > T) {
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -409,6 +430,23 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
     if (!rerun) break;
   }
 
+  if (piece >= 0) {  // unnormalised output, weight sum and shift of each query row
+    float *pp = part + ((int64_t)(L - full) * split + piece) * PIECE_FLOATS;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 16, 64);
+      l_tot += __shfl_xor(l_tot, 32, 64);
+      const int ql = wave * 32 + 16 * qb + r;  // query row within the item
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<f32x4 *>(pp + ql * 128 + 16 * db + 4 * g) = oacc[db][qb];
+      if (g == 0) {
+        pp[QT * 128 + ql] = l_tot;
+        pp[QT * 129 + ql] = -negm[qb][0];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 16, 64);
@@ -460,12 +498,106 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
 
 }  // namespace
 
+// Sum of the key-range pieces of split item full + blockIdx.x: with M the
+// largest of the pieces' shifts, O = sum_p O_p 2^(m_p - M) and
+// l = sum_p l_p 2^(m_p - M) (power-of-two scalings, exact in fp32), then
+// o = bf16(O * (1 / l)) as in the unsplit kernel. Because a power-of-two
+// scaling commutes with the bf16 rounding of the weights, this equals the
+// single-shift result up to the fp32 summation order. Thread u handles dims
+// 8 c .. 8 c + 7 of query row ql.
+__global__ __launch_bounds__(256) void attention_merge_kernel(const float *__restrict__ part,
+                                                              bf16 *__restrict__ o, int T, int H,
+                                                              int full, int split) {
+  const int L = full + (int)blockIdx.x;
+  const int qtiles = (int)ceil_div(T, QT);
+  const int h = L / qtiles, qt = L - h * qtiles;
+  const float *base = part + (int64_t)blockIdx.x * split * PIECE_FLOATS;
+  const int A = H * 128;
+  for (int u = threadIdx.x; u < QT * 16; u += 256) {
+    const int ql = u >> 4, c = u & 15;
+    const int q = qt * QT + ql;
+    if (q >= T) continue;
+    float M = -INFINITY;
+    for (int p = 0; p < split; ++p) M = fmaxf(M, base[p * PIECE_FLOATS + QT * 129 + ql]);
+    f32x4 a0 = {0.0f, 0.0f, 0.0f, 0.0f}, a1 = a0;
+    float l = 0.0f;
+    for (int p = 0; p < split; ++p) {
+      const float *pp = base + p * PIECE_FLOATS;
+      const float sc = ldexpf(1.0f, (int)(pp[QT * 129 + ql] - M));
+      const f32x4 v0 = *reinterpret_cast<const f32x4 *>(pp + ql * 128 + 8 * c);
+      const f32x4 v1 = *reinterpret_cast<const f32x4 *>(pp + ql * 128 + 8 * c + 4);
+      a0 += v0 * sc;
+      a1 += v1 * sc;
+      l += pp[QT * 128 + ql] * sc;
+    }
+    const float inv_l = 1.0f / l;
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[e] = to_bf16(a0[e] * inv_l);
+      out[4 + e] = to_bf16(a1[e] * inv_l);
+    }
+    *reinterpret_cast<bf16x8 *>(o + (int64_t)q * A + h * 128 + 8 * c) = out;
+  }
+}
+
+// Whole items first, then the last, partial round of items cut along the keys
+// into `split` pieces when that shortens it enough to pay for the pieces'
+// partial sums: cut into s, the rem items of the last round take
+// ceil(rem s / cus) rounds of 1/s of an item, and merging moves 266 KB per
+// piece through memory after the kernel (at about 5 TB/s, against an item's
+// time of about 26 ns per key: rem s 2.06 / T rounds); s = 1 unless the cut
+// saves a tenth of a round. (4096x4096 block: 112 items left, two pieces:
+// 0.53 instead of 1 round; 2048x2048: 184 left, no cut pays.)
+static int attention_split_plan(int T, int H, int *full, int *pieces_per_item) {
+  constexpr int cus = 256;  // MI355X compute units; one workgroup per CU
+  const int items = (int)ceil_div(T, QT) * H;
+  const int all_tiles = (int)ceil_div(T, KT);
+  const int rem = items % cus;
+  *full = items;
+  *pieces_per_item = 1;
+  if (rem == 0 || items < cus) return items;
+  double best = 1.0;
+  int bs = 1;
+  for (int sl = 2; sl <= 4 && 2 * sl <= all_tiles; ++sl) {
+    const double c = (double)ceil_div((int64_t)rem * sl, cus) / sl + (double)rem * sl * 2.06 / T;
+    if (c < best - 0.1) {
+      best = c;
+      bs = sl;
+    }
+  }
+  if (bs == 1) return items;
+  const int per = (int)ceil_div(all_tiles, bs);
+  bs = (int)ceil_div(all_tiles, per);  // every piece non-empty
+  *full = items - rem;
+  *pieces_per_item = bs;
+  return *full + rem * bs;
+}
+
+size_t attention_split_scratch_bytes(int T, int H) {
+  int full = 0, sl = 1;
+  attention_split_plan(T, H, &full, &sl);
+  const int items = (int)ceil_div(T, QT) * H;
+  return sl > 1 ? (size_t)(items - full) * sl * PIECE_FLOATS * sizeof(float) : 0;
+}
+
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
-                            hipStream_t s) {
-  dim3 grid((unsigned)(ceil_div(T, QT) * H));
-  hipLaunchKernelGGL(attention_kernel<false>, grid, dim3(NTHREADS), 0, s,
+                            hipStream_t s, float *part, size_t part_bytes) {
+  int full = 0, sl = 1;
+  int grid = attention_split_plan(T, H, &full, &sl);
+  const int items = (int)ceil_div(T, QT) * H;
+  if (sl > 1 && (!part || part_bytes < (size_t)(items - full) * sl * PIECE_FLOATS * sizeof(float))) {
+    sl = 1;  // no scratch for the pieces: whole items only
+    full = items;
+    grid = items;
+  }
+  hipLaunchKernelGGL(attention_kernel<false>, dim3((unsigned)grid), dim3(NTHREADS), 0, s,
                      static_cast<const bf16 *>(qk), static_cast<const bf16 *>(vt),
-                     static_cast<bf16 *>(o), nullptr, nullptr, T, H, Tp);
+                     static_cast<bf16 *>(o), nullptr, nullptr, T, H, Tp, part, full, sl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sl <= 1) return e;
+  hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)(items - full)), dim3(256), 0, s,
+                     part, static_cast<bf16 *>(o), T, H, full, sl);
   return hipGetLastError();
 }
 
@@ -474,7 +606,7 @@ hipError_t launch_attention_mx(const void *qk, const void *vt, void *o, uint8_t 
   dim3 grid((unsigned)(ceil_div(T, QT) * H));
   hipLaunchKernelGGL(attention_kernel<true>, grid, dim3(NTHREADS), 0, s,
                      static_cast<const bf16 *>(qk), static_cast<const bf16 *>(vt),
-                     static_cast<bf16 *>(o), o_codes, o_scales, T, H, Tp);
+                     static_cast<bf16 *>(o), o_codes, o_scales, T, H, Tp, nullptr, 0, 1);
   return hipGetLastError();
 }
 

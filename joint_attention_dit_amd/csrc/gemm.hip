@@ -46,12 +46,21 @@ namespace h3dit {
 
 namespace {
 
+#ifndef GEMM_NW
+#define GEMM_NW 8
+#endif
 constexpr int BK = 64;    // K per LDS stage (128-byte rows)
 constexpr int TILE_ELEMS = 256 * BK;  // one operand tile, bf16 elements (32 KB)
 
 
-template <int EPI>
-__global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
+// NW = 8: eight waves (two per SIMD) of 128 features x 64 tokens; NW = 4: four
+// waves (one per SIMD, 512 registers each) of 128 x 128, which reads 2/3 of
+// the LDS fragments per product.
+template <int EPI, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs a) {
+  constexpr int JB = 32 / NW;     // token blocks of 16 per wave
+  constexpr int CP = 32 / NW;     // 1 KB copy blocks per wave per operand tile
+  constexpr int NT = 64 * NW;
   // weight tiles: 2 stages of 32 KB; activation tiles: 3 stages of 32 KB (160 KB)
   __shared__ __attribute__((aligned(1024))) bf16 lds[5 * TILE_ELEMS];
 
@@ -81,10 +90,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
   // (l % 8) ^ swz(row). Rows past the matrix edge repeat the last row.
   const char *wpanel = static_cast<const char *>(a.w) + ((int64_t)n0 * a.K + kb0 * BK) * 2;
   const char *xpanel = static_cast<const char *>(a.x) + ((int64_t)t0 * a.K + kb0 * BK) * 2;
-  uint32_t woff[4], xoff[4];
+  uint32_t woff[CP], xoff[CP];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (wave * 4 + j) * 8 + (lane >> 3);
+  for (int j = 0; j < CP; ++j) {
+    const int row = (wave * CP + j) * 8 + (lane >> 3);
     const int lc = swz(row, lane & 7);
     woff[j] = (uint32_t)(min(n0 + row, a.N - 1) - n0) * (uint32_t)a.K * 2u + lc * 16u;
     xoff[j] = (uint32_t)(min(t0 + row, a.M - 1) - t0) * (uint32_t)a.K * 2u + lc * 16u;
@@ -94,13 +103,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
   // wst (activation stage xst)
   auto wload = [&](int wst, int k0, int j0, int j1) {
     const char *wp = wpanel + (int64_t)k0 * 2;
-    const uint32_t sw = lds0 + (uint32_t)(wst * TILE_ELEMS + wave * 4 * 512) * 2u;
+    const uint32_t sw = lds0 + (uint32_t)(wst * TILE_ELEMS + wave * CP * 512) * 2u;
 #pragma unroll
     for (int j = j0; j < j1; ++j) dma16(wp, woff[j], sw + j * 1024);
   };
   auto xload = [&](int xst, int k0, int j0, int j1) {
     const char *xp = xpanel + (int64_t)k0 * 2;
-    const uint32_t sx = lds0 + (uint32_t)((2 + xst) * TILE_ELEMS + wave * 4 * 512) * 2u;
+    const uint32_t sx = lds0 + (uint32_t)((2 + xst) * TILE_ELEMS + wave * CP * 512) * 2u;
 #pragma unroll
     for (int j = j0; j < j1; ++j) dma16(xp, xoff[j], sx + j * 1024);
   };
@@ -113,25 +122,25 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     fa_base[s] = (wn * 128 + r16) * BK + (swz(r16, 4 * s + kq) * 8);
-    fb_base[s] = (wt * 64 + r16) * BK + (swz(r16, 4 * s + kq) * 8);
+    fb_base[s] = (wt * 16 * JB + r16) * BK + (swz(r16, 4 * s + kq) * 8);
   }
 
-  f32x4 acc[8][4];
+  f32x4 acc[8][JB];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
 
   // A fragments are re-read in place once their four products have issued; B
   // fragments are double buffered
-  bf16x8 fa[8], fb[2][4];
+  bf16x8 fa[8], fb[2][JB];
   auto fload_all = [&](int wst, int xst, int s, int buf) {
     const bf16 *sw = lds + wst * TILE_ELEMS;
     const bf16 *sx = lds + (2 + xst) * TILE_ELEMS;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
       fb[buf][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[s] + j * 16 * BK);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -154,36 +163,57 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(fa[i], fb[BCUR][j], acc[i][j]);
+      for (int j = 0; j < JB; ++j) acc[i][j] = mfma16(fa[i], fb[BCUR][j], acc[i][j]);
       if constexpr (SYNC) {
         if (i == 0) {
           __builtin_amdgcn_sched_barrier(0);
           __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));
-          if (!RT || vm4) tile_barrier<4>();
+          if (!RT || vm4) tile_barrier<CP>();
           else tile_barrier<0>();
         }
-        if (i == 1 && (!RT || wref)) wload(kt & 1, (kt + 2) * BK, 0, 2);
-        if (i == 2 && (!RT || wref)) wload(kt & 1, (kt + 2) * BK, 2, 4);
-        if (i == 3 && (!RT || xref)) xload(xs, (kt + 3) * BK, 0, 2);
-        if (i == 4 && (!RT || xref)) xload(xs, (kt + 3) * BK, 2, 4);
+        if (i == 1 && (!RT || wref)) wload(kt & 1, (kt + 2) * BK, 0, CP / 2);
+        if (i == 2 && (!RT || wref)) wload(kt & 1, (kt + 2) * BK, CP / 2, CP);
+        if (i == 3 && (!RT || xref)) xload(xs, (kt + 3) * BK, 0, CP / 2);
+        if (i == 4 && (!RT || xref)) xload(xs, (kt + 3) * BK, CP / 2, CP);
       }
-      if (i == 0) {
+      if constexpr (NW == 8) {
+        if (i == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j)
+            fb[BCUR ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + j * 16 * BK);
+        }
+      } else if (i < 4) {  // two of the next k-step's B fragments per A block
+#pragma unroll
+        for (int j = 2 * i; j < 2 * i + 2; ++j)
           fb[BCUR ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + j * 16 * BK);
       }
       fa[i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + i * 16 * BK);
-      // the next k-step's B fragments two reads per two products, then one A
-      // fragment read per four products (measured: the fastest of the
-      // groupings tried)
-      if (i == 0) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if constexpr (NW == 8) {
+        // the next k-step's B fragments two reads per two products, then one A
+        // fragment read per four products (measured: the fastest of the
+        // groupings tried)
+        if (i == 0) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
       } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i < 4) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
       }
     }
   };
@@ -205,17 +235,17 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
           kt, xs);
   };
 
-  wload(0, 0, 0, 4);
-  xload(0, 0, 0, 4);
+  wload(0, 0, 0, CP);
+  xload(0, 0, 0, CP);
   if (ktiles > 1) {
-    wload(1, BK, 0, 4);
-    xload(1, BK, 0, 4);
+    wload(1, BK, 0, CP);
+    xload(1, BK, 0, CP);
   }
   if (ktiles > 2) {
-    xload(2, 2 * BK, 0, 4);
-    tile_barrier<12>();
+    xload(2, 2 * BK, 0, CP);
+    tile_barrier<3 * CP>();
   } else if (ktiles > 1) {
-    tile_barrier<8>();
+    tile_barrier<2 * CP>();
   } else {
     tile_barrier<0>();
   }
@@ -239,19 +269,19 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[(i * 4 + j) * 512] = acc[i][j];
+      for (int j = 0; j < JB; ++j) dst[(i * JB + j) * NT] = acc[i][j];
     return;
   }
   if constexpr (EPI == EPI_QKV_ROPE) {
     // every copy has landed and every wave has read its last fragments
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    staged_bf16_epilogue<EPI>(a, lds, acc, n0, t0, wn, wt, r16, kq);
+    staged_bf16_epilogue<EPI, JB, NT>(a, lds, acc, n0, t0, wn, wt, r16, kq);
     return;
   }
-  const int nb = n0 + wn * 128 + 4 * kq, tb = t0 + wt * 64 + r16;
+  const int nb = n0 + wn * 128 + 4 * kq, tb = t0 + wt * 16 * JB + r16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < JB; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       store4<EPI>(a, tb + 16 * j, nb + 16 * i, acc[i][j][0], acc[i][j][1], acc[i][j][2],
@@ -275,10 +305,10 @@ static hipError_t launch_epi(const GemmArgs &a0, hipStream_t s) {
   a.split = a.partial ? plan_split(a.M, a.N, a.K / BK, kPlanCus, a.partial_bytes, &rem) : 1;
   a.full_tiles = tiles - (a.split > 1 ? rem : 0);
   const int grid = a.split > 1 ? a.full_tiles + rem * a.split : tiles;
-  hipLaunchKernelGGL(gemm_kernel<EPI>, dim3(grid), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<EPI, GEMM_NW>), dim3(grid), dim3(64 * GEMM_NW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split <= 1) return e;
-  hipLaunchKernelGGL(gemm_fixup_kernel<EPI>, dim3(rem, 4), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((gemm_fixup_kernel<EPI, GEMM_NW>), dim3(rem, 4), dim3(64 * GEMM_NW), 0, s, a);
   return hipGetLastError();
 }
 

@@ -187,17 +187,19 @@ __device__ __forceinline__ int stage_off(int row, int col) {
 // instruction writes two contiguous 512-byte rows (instead of 2-byte scattered
 // stores for V). Used for the QKV epilogue (about 1.5 % faster there); the
 // GELU epilogue's direct 8-byte stores are as fast.
-template <int EPI>
-__device__ __forceinline__ void staged_bf16_epilogue(const GemmArgs &a, bf16 *lds, const f32x4 (&acc)[8][4],
+// JB: token blocks of 16 per wave (4: eight waves of 128 x 64, 8: four waves
+// of 128 x 128); NT threads per workgroup.
+template <int EPI, int JB = 4, int NT = 512>
+__device__ __forceinline__ void staged_bf16_epilogue(const GemmArgs &a, bf16 *lds, const f32x4 (&acc)[8][JB],
                                                      int n0, int t0, int wn, int wt, int r16, int kq) {
   const int tid = threadIdx.x;
   bool vtile = false;
   if constexpr (EPI == EPI_QKV_ROPE) vtile = n0 >= 2 * a.A;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < JB; ++j)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int tl = wt * 64 + 16 * j + r16, fl = wn * 128 + 16 * i + 4 * kq;
+      const int tl = wt * 16 * JB + 16 * j + r16, fl = wn * 128 + 16 * i + 4 * kq;
       const int t = t0 + tl, n = n0 + fl;
       const f32x4 v = acc[i][j];
       if constexpr (EPI == EPI_QKV_ROPE) {
@@ -216,7 +218,7 @@ __device__ __forceinline__ void staged_bf16_epilogue(const GemmArgs &a, bf16 *ld
     }
   __syncthreads();
 #pragma unroll 4
-  for (int q = tid; q < 256 * 32; q += 512) {
+  for (int q = tid; q < 256 * 32; q += NT) {
     const int row = q >> 5, c = q & 31;
     const bf16x8 val = *reinterpret_cast<const bf16x8 *>(lds + stage_off(row, 8 * c));
     if (vtile) {  // row = feature of the V tile, 8 tokens per chunk
@@ -248,10 +250,12 @@ __device__ __forceinline__ void tile_barrier() {
 }
 
 // Sum of the K slices of split tile full_tiles + blockIdx.x (in slice order),
-// then the epilogue, with the thread -> output mapping of gemm_kernel;
+// then the epilogue, with the thread -> output mapping of the GEMM kernel of
+// NW waves (partial sums stored [register block i * JB + j][thread]);
 // workgroup blockIdx.y takes feature blocks 2 y and 2 y + 1 of every wave.
-template <int EPI>
-__global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
+template <int EPI, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void gemm_fixup_kernel(GemmArgs a) {
+  constexpr int JB = 32 / NW, NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wt = wave >> 1;
   const int r16 = lane & 15, kq = lane >> 4;
@@ -260,12 +264,12 @@ __global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
   walk_coords(a.full_tiles + blockIdx.x, tiles_n, tiles_t, tn, tt);
   const f32x4 *src =
       reinterpret_cast<const f32x4 *>(a.partial) + (int64_t)blockIdx.x * a.split * (32 * 512) + tid;
-  const int nb = tn * BN + wn * 128 + 4 * kq, tb = tt * BT + wt * 64 + r16;
+  const int nb = tn * BN + wn * 128 + 4 * kq, tb = tt * BT + wt * 16 * JB + r16;
   if constexpr (EPI == EPI_GELU_MX) {  // feature blocks 2 y, 2 y + 1 are one block of 32
     const int i = 2 * (int)blockIdx.y;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t o0 = (i * 4 + j) * 512, o1 = ((i + 1) * 4 + j) * 512;
+    for (int j = 0; j < JB; ++j) {
+      const int64_t o0 = (i * JB + j) * NT, o1 = ((i + 1) * JB + j) * NT;
       f32x4 v0 = src[o0], v1 = src[o1];
       for (int sl = 1; sl < a.split; ++sl) {
         v0 += src[(int64_t)sl * (32 * 512) + o0];
@@ -276,11 +280,11 @@ __global__ __launch_bounds__(512) void gemm_fixup_kernel(GemmArgs a) {
     return;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < JB; ++j)
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int i = 2 * (int)blockIdx.y + ii;
-      const int64_t o = (i * 4 + j) * 512;
+      const int64_t o = (i * JB + j) * NT;
       f32x4 v = src[o];
       for (int sl = 1; sl < a.split; ++sl) v += src[(int64_t)sl * (32 * 512) + o];
       store4<EPI>(a, tb + 16 * j, nb + 16 * i, v[0], v[1], v[2], v[3]);

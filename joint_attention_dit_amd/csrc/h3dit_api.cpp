@@ -91,7 +91,7 @@ int check_config(const h3dit_config *cfg) {
 
 struct Plan {
   int64_t T, D, A, H, F, Tp;
-  size_t mod, table, h, qk, vt, o, x1, u, split, split_bytes, total;
+  size_t mod, table, h, qk, vt, o, x1, u, split, split_bytes, att, att_bytes, total;
   // MXFP8: codes and scales of the linears' inputs: region a holds h1, then o,
   // then h2; region b holds u (written while h2's codes are being read)
   size_t qa, qas, qb, qbs;
@@ -130,6 +130,9 @@ Plan make_plan(const h3dit_config *c, bool mx = false) {
   p.split_bytes = std::max(std::max(split_bytes(p.T, 3 * p.A, p.D), split_bytes(p.T, p.D, p.A)),
                            std::max(split_bytes(p.T, p.F, p.D), split_bytes(p.T, p.D, p.F)));
   p.split = take(p.split_bytes);
+  // key-range pieces of the attention's last round of workgroups (bf16 path)
+  p.att_bytes = mx ? 0 : attention_split_scratch_bytes((int)p.T, (int)p.H);
+  p.att = take(p.att_bytes);
   p.qa = p.qas = p.qb = p.qbs = 0;
   if (mx) {
     const int64_t ka = std::max(p.D, p.A);
@@ -281,7 +284,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
     LAUNCH(launch_attention_mx(qk, vt, lean ? nullptr : o, qa, qas, T, H, (int)p.Tp, s),
            "attention");
   else
-    LAUNCH(launch_attention(qk, vt, o, T, H, (int)p.Tp, s), "attention");
+    LAUNCH(launch_attention(qk, vt, o, T, H, (int)p.Tp, s, at<float>(ws, p.att), p.att_bytes),
+           "attention");
   LAUNCH(mark(5), "event record");
   {
     GemmArgs g = gemm_args(o, w->w_o, T, D, A);

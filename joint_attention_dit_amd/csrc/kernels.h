@@ -89,9 +89,12 @@ size_t gemm_mx_split_scratch_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_mxfp8_quantize(const void *x, int rows, int K, uint8_t *codes, uint8_t *scales,
                                  hipStream_t s);
 
-// o[T, A] = attention over qk [T, 2A] and vt [H, 128, Tp]
+// o[T, A] = attention over qk [T, 2A] and vt [H, 128, Tp]. With scratch
+// (part, at least attention_split_scratch_bytes(T, H) bytes) the last, partial
+// round of workgroups may be cut along the keys and merged by a second kernel.
 hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int H, int Tp,
-                            hipStream_t s);
+                            hipStream_t s, float *part = nullptr, size_t part_bytes = 0);
+size_t attention_split_scratch_bytes(int T, int H);
 // The same, o also as MXFP8 codes [T, H * 128] and scales (mxfp8_quantize layout);
 // o may be null (then only the codes and scales are written).
 hipError_t launch_attention_mx(const void *qk, const void *vt, void *o, uint8_t *o_codes,

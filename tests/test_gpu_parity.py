@@ -317,3 +317,38 @@ def test_block_deterministic():
     b = blk.forward().clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_attention_key_pieces_in_block():
+    """The block's attention when its last, partial round of workgroups is cut
+    along the keys (here 16 heads x 17 query tiles = 272 workgroups: 16 past
+    the first round of 256, each cut into key-range pieces whose partial sums
+    a second kernel merges, every piece with its own shift). o from the
+    block's workspace against the oracle's attention of the block's own q, k,
+    v on every row, and the block output against the oracle at the block bar."""
+    cfg = small_config("pieces", hidden=256, heads=16, ffn=512, text_tokens=44,
+                       images=((48, 89, 0),), x_dtype="bf16")
+    T, A, H = cfg.n_tokens, cfg.attn_width, cfg.heads
+    say(f"[block] attention key pieces T={T} H={H}")
+    inp = cached_case(cfg)
+    blk = B.Block(cfg, inp)
+    out = host(blk.forward())
+    it = blk.intermediates()
+    g_qk, g_vt, g_o = host(it["qk"]), unswap_vt(host(it["vt"])), host(it["o"])
+    q = g_qk[:, :A].reshape(T, H, 128)
+    k = g_qk[:, A:].reshape(T, H, 128)
+    v = g_vt[:, :, :T].transpose(2, 0, 1)
+    ref = O.attention(q, k, v, "contract").reshape(T, A)
+    e = errors(g_o, ref)
+    flip = np.empty_like(ref)
+    for h in range(H):
+        sc = q[:, h] @ k[:, h].T
+        P = O.bf16_round(np.exp2(sc - np.ceil(sc.max(axis=1, keepdims=True))))
+        flip[:, h * 128:(h + 1) * 128] = (P @ np.abs(v[:, h])) / P.sum(axis=1, keepdims=True)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bound = 2 * 2.0 ** -7 * np.abs(ref) + 2.0 ** -7 * (flip + np.abs(ref)) + 1e-4 * rms
+    excess = np.abs(g_o - ref) / bound
+    say(f"  o: rel_l2 {e['rel_l2']:.2e}, max err/bound {excess.max():.3f}")
+    assert e["rel_l2"] < 1e-3 and excess.max() <= 1.0
+    # (the pieces are head 15's query tiles 1..16, rows 256 .. T - 1 of its columns)
+    assert_block_parity(out, oracle_reference(cfg, inp)["out"], "pieces out")
