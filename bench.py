@@ -398,6 +398,52 @@ def measure_stack(scfg, images: int, warmup: int, mod_table: bool = True, linear
     return sec, ok
 
 
+def attention_inputs(T: int, H: int, rising: bool, seed: int = 0):
+    """Synthetic q (pre-scaled) and k, v in the attention kernel's layouts:
+    base-2 scores of standard deviation 12 (about that of the full-width
+    blocks), or with `rising` the keys' norms growing along the sequence
+    (x 0.2 .. 40), so that every row's largest score lies far past its first
+    key tile's and every workgroup takes the second pass of the kernel."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn(T, H * 128, device="cuda", generator=g) * (12.0 / 128 ** 0.5)
+    k = torch.randn(T, H * 128, device="cuda", generator=g)
+    if rising:
+        k *= (0.2 + 40.0 * torch.arange(T, device="cuda", dtype=torch.float32) / T).reshape(T, 1)
+    qk = torch.cat([q, k], dim=1).to(torch.bfloat16).contiguous()
+    vt = torch.randn(H, 128, T + (-T) % 64, device="cuda", generator=g).to(torch.bfloat16)
+    return qk, vt
+
+
+def measure_attention_cliff(cfg, steps: int, warmup: int):
+    """Time of h3dit_attention at the block's shape on ordinary scores and on
+    rising ones (every workgroup runs the key loop twice, after a scores-only
+    pass for its rows' maxima): the factor between the two bounds the cost of
+    the kernel's second pass."""
+    import torch
+    from joint_attention_dit_amd import binding as B
+
+    T, H = cfg.n_tokens, cfg.heads
+    c = B.make_config(cfg.hidden, H, cfg.ffn, T)
+    o = torch.empty(T, H * 128, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, rising in (("ordinary", False), ("rising", True)):
+        qk, vt = attention_inputs(T, H, rising)
+        for _ in range(warmup):
+            B.h3dit_attention(c, qk, vt, o, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            B.h3dit_attention(c, qk, vt, o, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+        del qk, vt
+    return res
+
+
 def measure_ulysses(cfg, G: int, steps: int, warmup: int):
     """One GPU's share of a block under G-way Ulysses sequence parallelism: the
     per-token kernels on T/G tokens (a block of T/G tokens with the same widths),
@@ -529,6 +575,8 @@ def main():
                     help="with --stack: compute each block's modulation per step instead of a table")
     ap.add_argument("--ulysses", type=int, default=0, metavar="G",
                     help="time one GPU's share of G-way Ulysses sequence parallelism instead")
+    ap.add_argument("--attention-cliff", action="store_true",
+                    help="time attention on ordinary vs rising scores (the kernel's second pass)")
     ap.add_argument("--traffic-run", action="store_true",
                     help="one 1 GiB copy + one block (the command the HBM counter passes profile)")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
@@ -563,6 +611,15 @@ def main():
     cfg = CONFIGS[args.workload]
     if args.traffic_run:
         traffic_run(cfg)
+        return
+    if args.attention_cliff:
+        r = measure_attention_cliff(cfg, max(args.steps // 2, 1), max(args.warmup // 2, 1))
+        print(json.dumps({
+            "metric": "attention time, ordinary scores vs scores rising along the sequence",
+            "value": round(r["rising"] / r["ordinary"], 3), "unit": "x (rising / ordinary)",
+            "n_gpus": 1, "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": cfg.description},
+            "ms": {k: round(v, 4) for k, v in r.items()}}), flush=True)
         return
     if args.ulysses:
         G = args.ulysses

@@ -34,10 +34,12 @@
 // running output is never rescaled. The loop only notes (in a wave-wide flag,
 // without a branch) whether some lane's sum of its 16 weights of a query in
 // some tile exceeded 2^76, i.e. a score more than about 104 above the first
-// tile's maximum. After the pass such a wave computes the exact maxima of its
-// rows (scores only, K read from global memory), and the workgroup runs the
-// whole key loop a second time, that wave's shifts raised to at least the
-// rounded-up row maxima. Every weight of the kept pass is at most 2^76.
+// tile's maximum. After the pass the workgroup then computes the exact maxima
+// of its rows (a scores-only pass, K streamed through LDS) and runs the whole
+// key loop a second time, its shifts raised to at least the rounded-up row
+// maxima. Every weight of the kept pass is at most 2^76. On scores that rise
+// along the sequence (every workgroup repeats) attention takes about 2.3x its
+// ordinary time.
 // Nothing in the common path touches the accumulated output outside the
 // matrix cores (a rescale of it inside the loop would not fit the registers).
 // Because scaling by a power of two commutes with bf16 rounding, the result
@@ -223,24 +225,6 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
       }
   };
 
-  // The same product with the K rows of tile `tile` read from global memory
-  // (its LDS stage is being refilled by then); only the rare path uses it.
-  auto scores_global = [&](int tile, auto d_c) {
-    constexpr int D = decltype(d_c)::value;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int row = min((kt0 + tile) * KT + 16 * b + r, T - 1);
-      const bf16 *kp = khead + (int64_t)row * ldqk + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(kp + 32 * s);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[D][b][qb] = mfma16(kf, qf[qb][s], s == 0 ? negm[qb] : sacc[D][b][qb]);
-      }
-    }
-  };
-
   // keys past T of tile `tile` get zero weight
   auto mask = [&](auto d_c, int tile) {
     constexpr int D = decltype(d_c)::value;
@@ -410,24 +394,33 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
       step(I0(), N(), it, again);
     }
     if (pass == 1) break;
-    if (again) {
-      // exact row maxima of this wave's queries, K read from global memory
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) negm[qb][v] = 0.0f;
-      for (int t = 0; t < ntiles; ++t) {
-        scores_global(t, I0());
-        mask(I0(), t);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) mrow[qb] = fmaxf(mrow[qb], tile_max(I0(), qb));
-      }
-    }
     // the workgroup runs pass 1 if any of its waves needs it (every wave
     // takes part in the tile copies and barriers)
     if (again && lane == 0) rerun = 1;
     __syncthreads();
     if (!rerun) break;
+    // Exact row maxima of every wave's queries for pass 1: a scores-only pass
+    // over the key tiles, streamed through the two K stages of LDS like the
+    // main loop (each tile copied once per workgroup; no weights, no P V).
+    // At the barrier of tile t, K(t) has landed and every wave is done with
+    // tile t - 1, whose stage then takes K(t + 1).
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) negm[qb][v] = 0.0f;
+    kload(0, 0);
+    for (int t = 0; t < ntiles; ++t) {
+      tile_barrier();
+      if (t + 1 < ntiles) kload((t + 1) & 1, t + 1);
+      if (t & 1)
+        scores(I1(), I0());
+      else
+        scores(I0(), I0());
+      mask(I0(), t);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) mrow[qb] = fmaxf(mrow[qb], tile_max(I0(), qb));
+    }
+    __syncthreads();  // every wave is done with the K stages before pass 1 refills them
   }
 
   if (piece >= 0) {  // unnormalised output, weight sum and shift of each query row

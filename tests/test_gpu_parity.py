@@ -352,3 +352,37 @@ def test_attention_key_pieces_in_block():
     assert e["rel_l2"] < 1e-3 and excess.max() <= 1.0
     # (the pieces are head 15's query tiles 1..16, rows 256 .. T - 1 of its columns)
     assert_block_parity(out, oracle_reference(cfg, inp)["out"], "pieces out")
+
+
+def test_attention_second_pass_cost_bounded():
+    """Scores that rise along the sequence make every workgroup find its rows'
+    maxima (a scores-only pass) and repeat the key loop: the kernel then takes
+    at most 2.6x its time on ordinary scores (about 1 + 0.3 + 1 passes). Times
+    are the fastest of five calls each, 4352 tokens, 16 heads."""
+    T, H = 4352, 16
+    say(f"[stage] attention second-pass cost T={T} H={H}")
+    c = B.make_config(256, H, 256, T)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    o = torch.empty(T, H * 128, dtype=torch.bfloat16, device="cuda")
+    times = {}
+    for rising in (False, True):
+        q = torch.randn(T, H * 128, device="cuda", generator=g) * (12.0 / 128 ** 0.5)
+        k = torch.randn(T, H * 128, device="cuda", generator=g)
+        if rising:
+            k *= (0.2 + 40.0 * torch.arange(T, device="cuda", dtype=torch.float32) / T).reshape(T, 1)
+        qk = torch.cat([q, k], dim=1).to(torch.bfloat16).contiguous()
+        vt = torch.randn(H, 128, T, device="cuda", generator=g).to(torch.bfloat16)
+        B.h3dit_attention(c, qk, vt, o)
+        best = float("inf")
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            B.h3dit_attention(c, qk, vt, o)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        assert torch.isfinite(o.float()).all()
+        times[rising] = best
+    ratio = times[True] / times[False]
+    say(f"  ordinary {times[False]:.3f} ms, rising {times[True]:.3f} ms: {ratio:.2f}x")
+    assert ratio <= 2.6
