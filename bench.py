@@ -239,22 +239,53 @@ def summarize_traffic(fetch_dir: str, write_dir: str, cfg) -> str:
     return "\n".join(lines) + "\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n"
 
 
-def _library_dispatches(rows):
+PERCENT_COUNTERS = ("MfmaUtil", "VALUBusy", "LdsUtil", "VALUUtilization", "GPU_UTIL")
+
+
+def _library_dispatches(rows, add_second: bool = True):
     """(dispatch id, kernel name, value) rows of the library's kernels in
-    dispatch order, a GEMM's slice-sum kernel merged into that GEMM, grouped
-    into block forwards of len(KERNEL_ORDER) kernels each."""
+    dispatch order, a GEMM's slice-sum kernel merged into that GEMM and the
+    attention's key-piece merge into the attention, grouped into block
+    forwards of len(KERNEL_ORDER) kernels each."""
     lib = []
     for r in sorted(rows):
         if "h3dit" not in r[1]:
             continue
-        if "gemm_fixup" in r[1]:
-            assert lib, "slice-sum kernel before any GEMM"
-            lib[-1] = (lib[-1][0], lib[-1][1], lib[-1][2] + r[2])
+        if "gemm_fixup" in r[1] or "attention_merge" in r[1]:
+            assert lib, "second kernel of a stage before its first"
+            if add_second:  # (a percentage of the main kernel is kept as it is)
+                lib[-1] = (lib[-1][0], lib[-1][1], lib[-1][2] + r[2])
         else:
             lib.append(r)
     n = len(KERNEL_ORDER)
     assert lib and len(lib) % n == 0, f"{len(lib)} library dispatches, not whole blocks of {n}"
     return [lib[i:i + n] for i in range(0, len(lib), n)]
+
+
+def _kernel_label(name: str) -> str:
+    """A profiler kernel name (mangled or not) -> 'h3dit::kernel<args>'."""
+    import subprocess
+
+    if name.startswith("_Z"):
+        try:
+            # GNU c++filt lacks the bf16 code DF16b: spell it as a vendor type
+            name = subprocess.run(["c++filt", name.replace("DF16b", "u6__bf16")],
+                                  capture_output=True, text=True,
+                                  check=False).stdout.strip() or name
+        except OSError:
+            pass
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):  # cut the parameter list
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
 
 
 def summarize_trace(trace_dir: str, warmup: int, cfg) -> str:
@@ -286,7 +317,7 @@ def summarize_trace(trace_dir: str, warmup: int, cfg) -> str:
             ach = f"{nbytes[stage] / (avg * 1e-6) / 1e9:.0f} GB/s"
             frac = nbytes[stage] / (avg * 1e-6) / 1e9 / PEAK_HBM_GBS
         rec[stage] = {"avg_us": round(avg, 2), "frac": round(frac, 4)}
-        lines.append(f"| `{blocks[0][i][1].split('(')[0]}` ({stage}) | {len(d)} | {avg:.1f} | "
+        lines.append(f"| `{_kernel_label(blocks[0][i][1])}` ({stage}) | {len(d)} | {avg:.1f} | "
                      f"{statistics.median(d):.1f} | {min(d):.1f} | {max(d):.1f} | {ach} | "
                      f"{100 * frac:.1f} % |")
     total = sum(sum(x[2] for x in b) for b in blocks) / len(blocks)
@@ -312,7 +343,7 @@ def summarize_counters(dirs, warmup: int) -> str:
                 by_counter.setdefault(r["Counter_Name"], []).append(
                     (int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
         for counter, rows in by_counter.items():
-            blocks = _library_dispatches(rows)[warmup:]
+            blocks = _library_dispatches(rows, counter not in PERCENT_COUNTERS)[warmup:]
             for i, stage in enumerate(KERNEL_ORDER):
                 per.setdefault(stage, {})[counter] = sum(b[i][2] for b in blocks) / len(blocks)
     counters = sorted({c for v in per.values() for c in v})
@@ -442,6 +473,36 @@ def measure_attention_cliff(cfg, steps: int, warmup: int):
         res[name] = e0.elapsed_time(e1) / steps
         del qk, vt
     return res
+
+
+def measure_gemm_reference(cfg, steps: int, warmup: int):
+    """Context only: the QKV-shaped product (T x 3A x D of the workload) through
+    this library's GEMM (h3dit_linear_f32, fp32 output) and through torch's
+    F.linear (hipBLASLt, bf16 output) on the same bf16 operands."""
+    import torch
+    import torch.nn.functional as F
+    from joint_attention_dit_amd import binding as B
+
+    M, N, K = cfg.n_tokens, 3 * cfg.attn_width, cfg.hidden
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, fn in (("h3dit_linear_f32", lambda: B.h3dit_linear_f32(x, w, y)),
+                     ("torch_linear_hipblaslt", lambda: F.linear(x, w))):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"ms": round(ms, 4), "tflops": round(2.0 * M * N * K / ms / 1e9, 1)}
+    return {"shape": [M, N, K], **res}
 
 
 def measure_ulysses(cfg, G: int, steps: int, warmup: int):
@@ -575,6 +636,8 @@ def main():
                     help="with --stack: compute each block's modulation per step instead of a table")
     ap.add_argument("--ulysses", type=int, default=0, metavar="G",
                     help="time one GPU's share of G-way Ulysses sequence parallelism instead")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="time the QKV-shaped GEMM here and through torch/hipBLASLt (context)")
     ap.add_argument("--attention-cliff", action="store_true",
                     help="time attention on ordinary vs rising scores (the kernel's second pass)")
     ap.add_argument("--traffic-run", action="store_true",
@@ -611,6 +674,11 @@ def main():
     cfg = CONFIGS[args.workload]
     if args.traffic_run:
         traffic_run(cfg)
+        return
+    if args.gemm_reference:
+        r = measure_gemm_reference(cfg, args.steps, max(args.warmup, 1))
+        print(json.dumps({"metric": "QKV-shaped GEMM time, this library vs hipBLASLt (context)",
+                          "config": {"workload": cfg.description}, **r}), flush=True)
         return
     if args.attention_cliff:
         r = measure_attention_cliff(cfg, max(args.steps // 2, 1), max(args.warmup // 2, 1))
