@@ -279,13 +279,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs a) {
     staged_bf16_epilogue<EPI, JB, NT>(a, lds, acc, n0, t0, wn, wt, r16, kq);
     return;
   }
-  const int nb = n0 + wn * 128 + 4 * kq, tb = t0 + wt * 16 * JB + r16;
-#pragma unroll
-  for (int j = 0; j < JB; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      store4<EPI>(a, tb + 16 * j, nb + 16 * i, acc[i][j][0], acc[i][j][1], acc[i][j][2],
-                  acc[i][j][3]);
+  direct_epilogue<EPI, JB>(a, acc, n0 + wn * 128 + 4 * kq, t0 + wt * 16 * JB + r16);
 }
 
 }  // namespace

@@ -59,11 +59,15 @@ __device__ __forceinline__ float gelu_tanh(float z) {
 // q or k: rotate the two adjacent pairs of the fp32 products, then round once;
 // q also takes the softmax factor log2(e)/sqrt(128) before its rounding, so that
 // attention scores leave the matrix cores in base-2 units.
-__device__ __forceinline__ bf16x4 qk_rope4(const GemmArgs &a, int t, int n, float v0, float v1,
-                                           float v2, float v3) {
-  const float u0 = v0, w0 = v1, u1 = v2, w1 = v3;
+// cos, sin of the two pairs of features n .. n + 3 (n % 4 == 0) of token t
+__device__ __forceinline__ f32x4 rope_cs4(const GemmArgs &a, int t, int n) {
   const int p = (n & 127) >> 1;  // pair index within the head (0..63)
-  const f32x4 cs = *reinterpret_cast<const f32x4 *>(a.table + ((int64_t)t * 64 + p) * 2);
+  return *reinterpret_cast<const f32x4 *>(a.table + ((int64_t)t * 64 + p) * 2);
+}
+
+__device__ __forceinline__ bf16x4 qk_rope4(const GemmArgs &a, int n, const f32x4 &cs, float v0,
+                                           float v1, float v2, float v3) {
+  const float u0 = v0, w0 = v1, u1 = v2, w1 = v3;
   const float sc = n < a.A ? kLog2eOverSqrt128 : 1.0f;
   bf16x4 r;
   r[0] = to_bf16((u0 * cs[0] - w0 * cs[1]) * sc);
@@ -99,7 +103,7 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
     if (n < A2) {
       if (t >= a.M) return;
       *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * A2 + n) =
-          qk_rope4(a, t, n, v0, v1, v2, v3);
+          qk_rope4(a, n, rope_cs4(a, t, n), v0, v1, v2, v3);
     } else {
       if (t >= a.Mp) return;
       const int hv = n - A2;  // head * 128 + dim
@@ -135,6 +139,60 @@ __device__ __forceinline__ void store4(const GemmArgs &a, int t, int n, float v0
     if (t >= a.M) return;
     *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(a.out) + (int64_t)t * a.N + n) =
         gelu4(v0, v1, v2, v3);
+  }
+}
+
+// The epilogue of a whole tile from registers (every epilogue but QKV's and
+// GELU_MX's): lane holds features nb + 16 i .. +3 of token tb + 16 j in
+// acc[i][j]. Each operand load is issued unconditionally (addresses clamped
+// into the matrix) and only the stores are predicated, so the residual rows of
+// eight feature blocks are in flight together instead of one per round trip
+// (a load guarded by the bounds branch of store4 waits for the previous
+// block's store). Same arithmetic as store4. N % 4 == 0.
+template <int EPI, int JB>
+__device__ __forceinline__ void direct_epilogue(const GemmArgs &a, const f32x4 (&acc)[8][JB], int nb,
+                                                int tb) {
+  if constexpr (EPI == EPI_RESID_BF16 || EPI == EPI_RESID_F32) {
+    float g[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int nc = min(nb + 16 * i, a.N - 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[i][e] = (float)a.gate[nc + e];
+    }
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      const int t = tb + 16 * j;
+      const int64_t row = (int64_t)min(t, a.M - 1) * a.N;
+      f32x4 rv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t off = row + min(nb + 16 * i, a.N - 4);
+        if constexpr (EPI == EPI_RESID_BF16) {
+          const bf16x4 rb = *reinterpret_cast<const bf16x4 *>(static_cast<const bf16 *>(a.resid) + off);
+          rv[i] = f32x4{(float)rb[0], (float)rb[1], (float)rb[2], (float)rb[3]};
+        } else {
+          rv[i] = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(a.resid) + off);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int n = nb + 16 * i;
+        if (t < a.M && n < a.N) {
+          f32x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = rv[i][e] + g[i][e] * acc[i][j][e];
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + (int64_t)t * a.N + n) = ov;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        store4<EPI>(a, tb + 16 * j, nb + 16 * i, acc[i][j][0], acc[i][j][1], acc[i][j][2],
+                    acc[i][j][3]);
   }
 }
 
@@ -196,26 +254,43 @@ __device__ __forceinline__ void staged_bf16_epilogue(const GemmArgs &a, bf16 *ld
   bool vtile = false;
   if constexpr (EPI == EPI_QKV_ROPE) vtile = n0 >= 2 * a.A;
 #pragma unroll
-  for (int j = 0; j < JB; ++j)
+  for (int j = 0; j < JB; ++j) {
+    const int tl = wt * 16 * JB + 16 * j + r16, t = t0 + tl;
+    if constexpr (EPI == EPI_QKV_ROPE) {
+      if (vtile) {
+        const bool live = t < a.M;
+        const int col = vt_col(tl);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tl = wt * 16 * JB + 16 * j + r16, fl = wn * 128 + 16 * i + 4 * kq;
-      const int t = t0 + tl, n = n0 + fl;
-      const f32x4 v = acc[i][j];
-      if constexpr (EPI == EPI_QKV_ROPE) {
-        if (vtile) {
-          const bool live = t < a.M;
-          const int col = vt_col(tl);
+        for (int i = 0; i < 8; ++i) {
+          const int fl = wn * 128 + 16 * i + 4 * kq;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lds[stage_off(fl + e, col)] = to_bf16(live ? v[e] : 0.0f);
-          continue;
+          for (int e = 0; e < 4; ++e)
+            lds[stage_off(fl + e, col)] = to_bf16(live ? acc[i][j][e] : 0.0f);
         }
-        const bf16x4 r = t < a.M ? qk_rope4(a, t, n, v[0], v[1], v[2], v[3]) : bf16x4{};
+        continue;
+      }
+      // the eight table entries of this token block are loaded together
+      // (token clamped into the table), then rotated
+      f32x4 cs[8];
+      const int tc = min(t, a.M - 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cs[i] = rope_cs4(a, tc, n0 + wn * 128 + 16 * i + 4 * kq);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int fl = wn * 128 + 16 * i + 4 * kq;
+        const f32x4 v = acc[i][j];
+        const bf16x4 r = t < a.M ? qk_rope4(a, n0 + fl, cs[i], v[0], v[1], v[2], v[3]) : bf16x4{};
         *reinterpret_cast<bf16x4 *>(lds + stage_off(tl, fl)) = r;
-      } else {
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int fl = wn * 128 + 16 * i + 4 * kq;
+        const f32x4 v = acc[i][j];
         *reinterpret_cast<bf16x4 *>(lds + stage_off(tl, fl)) = gelu4(v[0], v[1], v[2], v[3]);
       }
     }
+  }
   __syncthreads();
 #pragma unroll 4
   for (int q = tid; q < 256 * 32; q += NT) {

@@ -303,12 +303,7 @@ __global__ __launch_bounds__(512, 1) void gemm_mx_kernel(GemmArgs a) {
         gelu_mx_block(a, tb + 16 * j, nb + 32 * m, kq, acc[2 * m][j], acc[2 * m + 1][j]);
     return;
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      store4<EPI>(a, tb + 16 * j, nb + 16 * i, acc[i][j][0], acc[i][j][1], acc[i][j][2],
-                  acc[i][j][3]);
+  direct_epilogue<EPI, 4>(a, acc, nb, tb);
 }
 
 }  // namespace
