@@ -354,6 +354,52 @@ def test_attention_key_pieces_in_block():
     assert_block_parity(out, oracle_reference(cfg, inp)["out"], "pieces out")
 
 
+@pytest.mark.slow
+def test_attention_shift_rise_full_length_rows():
+    """The second pass at the full 4096x4096 sequence length (16,896 tokens,
+    8 heads: 528 workgroups, the last partial round cut into key-range pieces
+    when the split plan takes it): keys whose norm grows along the sequence,
+    so every workgroup finds its rows' maxima and runs its key loop again.
+    Against the oracle on 256 seeded query rows over all keys, with the
+    per-element bound of the short-sequence shift tests."""
+    T, H = 16896, 8
+    say(f"[stage] attention shift rise full length T={T} H={H}")
+    g = torch.Generator().manual_seed(12)
+    q = torch.randn(T, H, 128, generator=g) * (12.0 / 128 ** 0.5)
+    k = torch.randn(T, H, 128, generator=g)
+    k *= (0.2 + 40.0 * torch.arange(T, dtype=torch.float32) / T).reshape(T, 1, 1)
+    v = torch.randn(T, H, 128, generator=g)
+    qb, kb, vb = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    del q, k, v
+    Tp = B.h3dit_padded_tokens(T)
+    qk = torch.cat([qb.reshape(T, H * 128), kb.reshape(T, H * 128)], dim=1).contiguous().cuda()
+    vt = _vt_from_tokens(vb, Tp).cuda()
+    o = torch.empty(T, H * 128, dtype=torch.bfloat16, device="cuda")
+    B.h3dit_attention(B.make_config(256, H, 256, T), qk, vt, o)
+    torch.cuda.synchronize()
+    rows = sample_rows(T, 256, seed=1)
+    f = lambda t: t.to(torch.float64).numpy()
+    fq, fk, fv = f(qb[rows]), f(kb), f(vb)
+    first = max(float((fq[:, h] @ fk[:64, h].T).max()) for h in range(H))
+    s_max = max(float((fq[:, h] @ fk[:, h].T).max()) for h in range(H))
+    say(f"  max score {s_max:.1f}, first tile max {first:.1f}")
+    assert s_max > first + 130, "the case must push scores far past the first tile"
+    ref = O.attention(fq, fk, fv, "contract").reshape(len(rows), H * 128)
+    got = host(o)[rows]
+    e = errors(got, ref)
+    flip = np.empty_like(ref)
+    for h in range(H):
+        sc = fq[:, h] @ fk[:, h].T
+        P = O.bf16_round(np.exp2(sc - np.ceil(sc.max(axis=1, keepdims=True))))
+        flip[:, h * 128:(h + 1) * 128] = (P @ np.abs(fv[:, h])) / P.sum(axis=1, keepdims=True)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bound = 2 * 2.0 ** -7 * np.abs(ref) + 2.0 ** -7 * (flip + np.abs(ref)) + 1e-4 * rms
+    excess = np.abs(got - ref) / bound
+    say(f"  o: rel_l2 {e['rel_l2']:.2e}, max err/bound {excess.max():.3f}")
+    assert np.all(np.isfinite(got)) and e["rel_l2"] < 1e-3
+    assert excess.max() <= 1.0
+
+
 def test_attention_second_pass_cost_bounded():
     """Scores that rise along the sequence make every workgroup find its rows'
     maxima (a scores-only pass) and repeat the key loop: the kernel then takes
