@@ -46,21 +46,15 @@ namespace h3dit {
 
 namespace {
 
-#ifndef GEMM_NW
-#define GEMM_NW 8
-#endif
 constexpr int BK = 64;    // K per LDS stage (128-byte rows)
 constexpr int TILE_ELEMS = 256 * BK;  // one operand tile, bf16 elements (32 KB)
+constexpr int NW = 8;     // waves per workgroup (two per SIMD) of 128 features x 64 tokens
+constexpr int JB = 4;     // token blocks of 16 per wave
+constexpr int CP = 4;     // 1 KB copy blocks per wave per operand tile
+constexpr int NT = 64 * NW;
 
-
-// NW = 8: eight waves (two per SIMD) of 128 features x 64 tokens; NW = 4: four
-// waves (one per SIMD, 512 registers each) of 128 x 128, which reads 2/3 of
-// the LDS fragments per product.
-template <int EPI, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs a) {
-  constexpr int JB = 32 / NW;     // token blocks of 16 per wave
-  constexpr int CP = 32 / NW;     // 1 KB copy blocks per wave per operand tile
-  constexpr int NT = 64 * NW;
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(GemmArgs a) {
   // weight tiles: 2 stages of 32 KB; activation tiles: 3 stages of 32 KB (160 KB)
   __shared__ __attribute__((aligned(1024))) bf16 lds[5 * TILE_ELEMS];
 
@@ -176,44 +170,23 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs a) {
         if (i == 3 && (!RT || xref)) xload(xs, (kt + 3) * BK, 0, CP / 2);
         if (i == 4 && (!RT || xref)) xload(xs, (kt + 3) * BK, CP / 2, CP);
       }
-      if constexpr (NW == 8) {
-        if (i == 0) {
+      if (i == 0) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            fb[BCUR ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + j * 16 * BK);
-        }
-      } else if (i < 4) {  // two of the next k-step's B fragments per A block
-#pragma unroll
-        for (int j = 2 * i; j < 2 * i + 2; ++j)
+        for (int j = 0; j < JB; ++j)
           fb[BCUR ^ 1][j] = *reinterpret_cast<const bf16x8 *>(sx + fb_base[ns] + j * 16 * BK);
       }
       fa[i] = *reinterpret_cast<const bf16x8 *>(sw + fa_base[ns] + i * 16 * BK);
-      if constexpr (NW == 8) {
-        // the next k-step's B fragments two reads per two products, then one A
-        // fragment read per four products (measured: the fastest of the
-        // groupings tried)
-        if (i == 0) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+      // the next k-step's B fragments two reads per two products, then one A
+      // fragment read per four products (measured: the fastest of the
+      // groupings tried)
+      if (i == 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       } else {
-        if (i < 4) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
   };
@@ -299,10 +272,10 @@ static hipError_t launch_epi(const GemmArgs &a0, hipStream_t s) {
   a.split = a.partial ? plan_split(a.M, a.N, a.K / BK, kPlanCus, a.partial_bytes, &rem) : 1;
   a.full_tiles = tiles - (a.split > 1 ? rem : 0);
   const int grid = a.split > 1 ? a.full_tiles + rem * a.split : tiles;
-  hipLaunchKernelGGL((gemm_kernel<EPI, GEMM_NW>), dim3(grid), dim3(64 * GEMM_NW), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<EPI>), dim3(grid), dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split <= 1) return e;
-  hipLaunchKernelGGL((gemm_fixup_kernel<EPI, GEMM_NW>), dim3(rem, 4), dim3(64 * GEMM_NW), 0, s, a);
+  hipLaunchKernelGGL((gemm_fixup_kernel<EPI, NW>), dim3(rem, 4), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
