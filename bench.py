@@ -673,8 +673,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the block runs on a single MI355X and this build "
-              "has no multi-GPU path (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the block runs on a single MI355X; there is no "
+              "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch

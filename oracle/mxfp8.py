@@ -18,7 +18,7 @@ module follows the public OCP definitions of it:
     largest magnitude a > 0, X = floor(log2(a)) - 8, where 8 is the largest
     exponent of E4M3; each element is stored as e4m3(v / 2**X).
 
-Readings where the definitions leave a choice (listed in the design doc): the
+Readings where the definitions leave a choice: the
 element conversion rounds to nearest with ties to even and saturates to
 +-448 (a block's largest element can exceed 448 after scaling by at most a
 factor 512/448); a block of zeros takes X = -127; a negative value that
