@@ -119,7 +119,9 @@ int h3dit_block_forward(const h3dit_config *cfg, const void *x, const float *con
  * (256 MiB) that each GPU the library runs on holds until the process ends.
  * The call allocates nothing. Shapes whose h3dit_workspace_size() exceeds
  * that size return H3DIT_EWORKSPACE before any HIP call (at full width,
- * hidden 5376, that is above about 1,500 tokens). The array belongs to the
+ * hidden 5376, from 1,521 tokens on, though some larger counts fit again as
+ * the GEMMs' K-slice scratch varies with the token count:
+ * h3dit_workspace_size() decides). The array belongs to the
  * current device (hipSetDevice), which must be the device of `stream`; calls
  * on one GPU share it, so two calls that overlap in time on the same GPU (on
  * different streams, or from different threads) race: order them on one
