@@ -75,3 +75,24 @@ def test_block_full_width_sampled_rows(name):
     say(f"[exact] {name}: GPU vs exact rel_l2={e_gpu['rel_l2']:.3e} "
         f"max_abs/rms={e_gpu['max_abs_over_rms']:.3e}; contract vs exact "
         f"rel_l2={e_con['rel_l2']:.3e} max_abs/rms={e_con['max_abs_over_rms']:.3e}")
+
+
+@pytest.mark.parametrize("input_seed", [1, 2])
+def test_block_4096_other_input_seeds(input_seed):
+    """The 4096x4096 block on other seeded inputs (weights, x and cond drawn
+    with another seed), on the seed-1 rows: the relative-L2 bar must hold;
+    the max |err| / RMS is printed, not asserted (it is the tail of the bf16
+    re-rounding noise described above, and moves with the data as it moves
+    with the row sample)."""
+    cfg = CONFIGS["4096"]
+    say(f"[block] 4096 input seed {input_seed}")
+    inp = make_inputs(cfg, seed=input_seed)
+    got, blk = run_block(cfg, inp)
+    del blk
+    torch.cuda.empty_cache()
+    rows = sample_rows(cfg.n_tokens, 256, seed=1)
+    ref = oracle_reference(cfg, inp, rows=rows)["out"]
+    e = errors(got[rows], ref)
+    say(f"[parity] 4096 input seed {input_seed}: rel_l2={e['rel_l2']:.3e} "
+        f"max_abs/rms={e['max_abs_over_rms']:.3e} (max-abs not asserted)")
+    assert np.all(np.isfinite(got[rows])) and e["rel_l2"] <= REL_L2
