@@ -98,10 +98,15 @@ def measure(cfg, steps: int, warmup: int, linears: str = "bf16"):
     ms = start.elapsed_time(end) / steps
     stage_ms = {s: sum(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)) / steps
                 for i, s in enumerate(STAGES)}
+    # each block forward on its own, first to last stage event: spread over the timed steps
+    per_step = sorted(ev[k][0].elapsed_time(ev[k][-1]) for k in range(steps))
+    spread = {"median_ms": round(per_step[steps // 2] if steps % 2 else
+                                 0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2]), 4),
+              "min_ms": round(per_step[0], 4), "max_ms": round(per_step[-1], 4)}
     out_ok = bool(torch.isfinite(blk.out).all().item())
     del blk
     torch.cuda.empty_cache()
-    return ms, stage_ms, out_ok
+    return ms, stage_ms, out_ok, spread
 
 
 def summarize(cfg, ms, stage_ms, linears: str = "bf16"):
@@ -540,7 +545,7 @@ def measure_ulysses(cfg, G: int, steps: int, warmup: int):
                                     images=((rows, cols, 0),),
                                     description=f"{cfg.name} share of {G}: {text} text + {rows}x{cols} image tokens")
     assert share.n_tokens == Ts, (share.n_tokens, Ts)
-    ms, stage_ms, ok = measure(share, steps, warmup)
+    ms, stage_ms, ok, _ = measure(share, steps, warmup)
 
     # attention of the share: Hs heads over all T tokens
     acfg = B.make_config(cfg.hidden, Hs, cfg.ffn, T)
@@ -730,7 +735,7 @@ def main():
             "pct_bf16_mfma_peak": round(100 * fl / sec / 1e12 / PEAK_BF16_TFLOPS, 2),
             "output_finite": ok}), flush=True)
         return
-    ms, stage_ms, ok = measure(cfg, args.steps, args.warmup, args.linears)
+    ms, stage_ms, ok, spread = measure(cfg, args.steps, args.warmup, args.linears)
     tflops, kernels, roof = summarize(cfg, ms, stage_ms, args.linears)
 
     rec = {
@@ -741,6 +746,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "per_step": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -759,11 +765,11 @@ def main():
     }
     if args.extra not in ("", "none") and args.extra != args.workload:
         ecfg = CONFIGS[args.extra]
-        ems, est, eok = measure(ecfg, max(args.steps // 2, 1), max(args.warmup // 2, 1),
+        ems, est, eok, espread = measure(ecfg, max(args.steps // 2, 1), max(args.warmup // 2, 1),
                                 args.linears)
         etf, ekern, eroof = summarize(ecfg, ems, est, args.linears)
         rec["extra"] = {"workload": ecfg.description, "n_tokens": ecfg.n_tokens,
-                        "ms_per_step": round(ems, 4), "value": round(ecfg.n_tokens / (ems * 1e-3), 1),
+                        "ms_per_step": round(ems, 4), "per_step": espread, "value": round(ecfg.n_tokens / (ems * 1e-3), 1),
                         "unit": "block-tokens/s", "tflops": round(etf, 1),
                         "pct_bf16_mfma_peak": round(100 * etf / PEAK_BF16_TFLOPS, 2),
                         "kernels": ekern}
