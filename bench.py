@@ -159,10 +159,28 @@ COPY_BYTES = 1 << 30   # the plain copy used to calibrate the HBM byte counters
 
 
 def source_digest(stage: str) -> str:
+    """Digest of the kernel's source file and of every local header it includes
+    (recursively, in include order), so that a change to a shared header also
+    marks the stored counter figures as stale."""
     import hashlib
-    path = os.path.join(ROOT, "joint_attention_dit_amd", "csrc", KERNEL_SOURCES[stage])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    import re
+    csrc = os.path.join(ROOT, "joint_attention_dit_amd", "csrc")
+    h = hashlib.sha256()
+    seen = set()
+
+    def add(name):
+        path = os.path.join(csrc, name)
+        if name in seen or not os.path.exists(path):
+            return
+        seen.add(name)
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(name.encode() + b"\0" + data)
+        for inc in re.findall(rb'^#include "([^"]+)"', data, re.M):
+            add(inc.decode())
+
+    add(KERNEL_SOURCES[stage])
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(stage: str):
