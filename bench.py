@@ -360,15 +360,32 @@ def summarize_trace(trace_dir: str, warmup: int, cfg, linears: str = "bf16") -> 
     return "\n".join(lines) + "\n\n```json\n" + json.dumps(rec, indent=1) + "\n```\n"
 
 
-def summarize_counters(dirs, warmup: int) -> str:
+def summarize_counters(dirs, warmup: int, cfg=None) -> str:
     """Counter CSVs of `bench.py --extra=none` runs under rocprofv3 --pmc (one
     directory per pass) -> per-kernel averages over the timed block forwards
-    (the first `warmup` dropped). A GEMM's slice-sum kernel adds into the GEMM."""
+    (the first `warmup` dropped). A GEMM's slice-sum kernel adds into the GEMM.
+    With `cfg`, a table of the matrix-core kernels comes first: the clock they
+    ran at (GRBM_GUI_ACTIVE over the 8 XCDs and the dispatches' own durations in
+    the pass that counted it) and their rate against the peak at that clock."""
     import csv
     import glob
 
     per = {}
+    dur = {}  # stage -> average duration (ns) in the pass that counted GRBM_GUI_ACTIVE
     for d in dirs:
+        trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+        counted = set()
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            counted |= {r["Counter_Name"] for r in csv.DictReader(open(f))}
+        if trace and "GRBM_GUI_ACTIVE" in counted and not dur:
+            rows = []
+            for f in trace:
+                for r in csv.DictReader(open(f)):
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                 float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))))
+            blocks = _library_dispatches(rows)[warmup:]
+            for i, stage in enumerate(KERNEL_ORDER):
+                dur[stage] = sum(b[i][2] for b in blocks) / len(blocks)
         by_counter = {}
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
@@ -379,7 +396,28 @@ def summarize_counters(dirs, warmup: int) -> str:
             for i, stage in enumerate(KERNEL_ORDER):
                 per.setdefault(stage, {})[counter] = sum(b[i][2] for b in blocks) / len(blocks)
     counters = sorted({c for v in per.values() for c in v})
-    lines = ["| Kernel | " + " | ".join(counters) + " |", "|---|" + "---|" * len(counters)]
+    lines = []
+    need = ("MfmaUtil", "VALUBusy", "LdsUtil", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS",
+            "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+    if cfg is not None and dur and all(c in counters for c in need):
+        flops, _ = stage_work(cfg)
+        lines += ["| Kernel | MfmaUtil (%) | VALUBusy (%) | LdsUtil (%) | LDS bank-conflict cycles "
+                  "/ LDS instr. | MFMA-VALU co-issue cycles / MFMA busy cycles | clock under load "
+                  "(GHz) | duration in the pass (us) | TFLOP/s | of the peak at that clock |",
+                  "|---|---|---|---|---|---|---|---|---|---|"]
+        for stage in KERNEL_ORDER:
+            c = per[stage]
+            if stage not in GEMM_STAGES and stage != "attention":
+                continue
+            ghz = c["GRBM_GUI_ACTIVE"] / 8 / dur[stage]
+            tf = flops[stage] / (dur[stage] * 1e-9) / 1e12
+            at_clock = PEAK_BF16_TFLOPS * ghz / 2.4
+            lines.append(f"| {stage} | {c['MfmaUtil']:.1f} | {c['VALUBusy']:.1f} | {c['LdsUtil']:.1f} | "
+                         f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_INSTS_LDS'], 1):.3f} | "
+                         f"{c['SQ_VALU_MFMA_COEXEC_CYCLES'] / max(c['SQ_VALU_MFMA_BUSY_CYCLES'], 1):.3f} | "
+                         f"{ghz:.2f} | {dur[stage] * 1e-3:.1f} | {tf:.0f} | {100 * tf / at_clock:.1f} % |")
+        lines.append("")
+    lines += ["| Kernel | " + " | ".join(counters) + " |", "|---|" + "---|" * len(counters)]
     for stage in KERNEL_ORDER:
         lines.append(f"| {stage} | " + " | ".join(f"{per[stage].get(c, float('nan')):.4g}"
                                                   for c in counters) + " |")
@@ -688,7 +726,8 @@ def main():
                               args.linears))
         return
     if args.summarize_counters:
-        print(summarize_counters(args.summarize_counters, args.warmup))
+        from joint_attention_dit_amd.inputs import CONFIGS
+        print(summarize_counters(args.summarize_counters, args.warmup, CONFIGS[args.workload]))
         return
     if args.summarize_traffic:
         from joint_attention_dit_amd.inputs import CONFIGS
