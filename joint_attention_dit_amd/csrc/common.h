@@ -33,6 +33,14 @@ __device__ __forceinline__ bf16x2 pack2(float a, float b) {
 
 __device__ __forceinline__ float bf16_round_f32(float v) { return (float)(bf16)v; }
 
+// Load of data that one kernel reads once (weights of a GEMV, rows of a
+// normalisation): the nontemporal hint lets the caches drop the line instead of
+// keeping it over data that is reused.
+template <typename T>
+__device__ __forceinline__ T load_once(const T *p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // 32x32x16 bf16 matrix-core product with fp32 accumulation.
 // Lane l supplies A[l % 32][8 * (l / 32) .. +7] and B[8 * (l / 32) .. +7][l % 32];
 // it receives C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32] in element i.

@@ -25,8 +25,9 @@ struct Chunk8;
 template <>
 struct Chunk8<bf16> {
   typedef bf16x8 raw;
+  // the block's input rows: read once, with the nontemporal hint
   static __device__ __forceinline__ raw fetch(const bf16 *p) {
-    return *reinterpret_cast<const bf16x8 *>(p);
+    return load_once(reinterpret_cast<const bf16x8 *>(p));
   }
   static __device__ __forceinline__ float at(const raw &r, int j) { return (float)r[j]; }
   static __device__ __forceinline__ void load(const bf16 *p, float v[8]) {
@@ -41,6 +42,9 @@ struct Chunk8<float> {
   struct raw {
     f32x4 a, b;
   };
+  // plain loads: fp32 rows are the residual stream that the previous kernel has
+  // just written, partly still in the last-level cache (the nontemporal hint
+  // measured 2-14 % slower on them)
   static __device__ __forceinline__ raw fetch(const float *p) {
     return raw{*reinterpret_cast<const f32x4 *>(p), *reinterpret_cast<const f32x4 *>(p + 4)};
   }
