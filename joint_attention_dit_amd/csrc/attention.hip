@@ -501,8 +501,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attention_kernel(const bf16 *__re
 // l = sum_p l_p 2^(m_p - M) (power-of-two scalings, exact in fp32), then
 // o = bf16(O * (1 / l)) as in the unsplit kernel. Because a power-of-two
 // scaling commutes with the bf16 rounding of the weights, this equals the
-// single-shift result up to the fp32 summation order. Thread u handles dims
-// 8 c .. 8 c + 7 of query row ql.
+// single-shift result up to the fp32 summation order. Workgroup (x, y) takes
+// query rows 64 y .. 64 y + 63 of the item (four workgroups per item, so that
+// enough waves are in flight); thread u handles dims 8 c .. 8 c + 7 of query
+// row ql.
 __global__ __launch_bounds__(256) void attention_merge_kernel(const float *__restrict__ part,
                                                               bf16 *__restrict__ o, int T, int H,
                                                               int full, int split) {
@@ -511,7 +513,8 @@ __global__ __launch_bounds__(256) void attention_merge_kernel(const float *__res
   const int h = L / qtiles, qt = L - h * qtiles;
   const float *base = part + (int64_t)blockIdx.x * split * PIECE_FLOATS;
   const int A = H * 128;
-  for (int u = threadIdx.x; u < QT * 16; u += 256) {
+  for (int u = (int)blockIdx.y * 64 * 16 + threadIdx.x; u < ((int)blockIdx.y + 1) * 64 * 16;
+       u += 256) {
     const int ql = u >> 4, c = u & 15;
     const int q = qt * QT + ql;
     if (q >= T) continue;
@@ -594,7 +597,7 @@ hipError_t launch_attention(const void *qk, const void *vt, void *o, int T, int 
                      static_cast<bf16 *>(o), nullptr, nullptr, T, H, Tp, part, full, sl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sl <= 1) return e;
-  hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)(items - full)), dim3(256), 0, s,
+  hipLaunchKernelGGL(attention_merge_kernel, dim3((unsigned)(items - full), QT / 64), dim3(256), 0, s,
                      part, static_cast<bf16 *>(o), T, H, full, sl);
   return hipGetLastError();
 }
