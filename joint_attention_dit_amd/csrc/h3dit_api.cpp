@@ -168,9 +168,12 @@ GemmArgs gemm_args(const void *x, const void *w, int64_t M, int64_t N, int64_t K
 int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, const h3dit_weights *w,
                  const int32_t *positions, float *out, void *ws, size_t ws_bytes, void *stream,
                  void *const *events, int n_events, const double *mod_in = nullptr,
-                 const h3dit_mxfp8_weights *q = nullptr, bool lean = false) {
+                 const h3dit_mxfp8_weights *q = nullptr, bool lean = false,
+                 bool table_ready = false) {
   // lean (MXFP8 only): the producers write only the codes the next linear
-  // consumes, not the bf16 copies of h1, o, h2 and u kept for inspection
+  // consumes, not the bf16 copies of h1, o, h2 and u kept for inspection.
+  // table_ready: the workspace's RoPE table region already holds the table of
+  // these positions (the DiT stack computes it once for all its blocks).
   CHECK_CFG(cfg);
   if (!w) return fail(H3DIT_EINVAL, "w is NULL");
   CHECK_PTR(x);
@@ -257,7 +260,8 @@ int forward_impl(const h3dit_config *cfg, const void *x, const float *cond, cons
   if (!mod_in)
     LAUNCH(launch_modulation(w->w_ada, cond, at<double>(ws, p.mod), 6 * D, D, s), "modulation");
   LAUNCH(mark(1), "event record");
-  LAUNCH(launch_rope_table(positions, table, T, cfg->rope_base, s), "rope table");
+  if (!table_ready)
+    LAUNCH(launch_rope_table(positions, table, T, cfg->rope_base, s), "rope table");
   LAUNCH(mark(2), "event record");
   if (q)  // h1 in bf16 and as MXFP8 codes for the QKV linear
     LAUNCH(launch_rmsnorm_modulate_mx(x, cfg->x_dtype == H3DIT_F32, mod + 0 * D, mod + 1 * D, h, qa,
@@ -450,14 +454,20 @@ int dit_impl(const h3dit_config *cfg, const h3dit_stack_config *st, const h3dit_
          "patchify");
   LAUNCH(launch_gemm_f32(patches, w->w_patch, xa + (size_t)text_tokens * D, Ti, D, F, D, s),
          "patch embedding");
-  // the blocks, ping-ponging the fp32 residual stream
+  // the blocks, ping-ponging the fp32 residual stream; every block uses the same
+  // positions, so the RoPE table is made once, in the block workspace's table region
   const h3dit_config bc = stack_block_config(cfg);
+  if (st->n_blocks > 0)
+    LAUNCH(launch_rope_table(positions,
+                             at<float>(at<void>(ws, p.block), make_plan(&bc, q != nullptr).table),
+                             bc.n_tokens, bc.rope_base, s),
+           "rope table");
   float *cur = xa, *nxt = xb;
   for (int l = 0; l < st->n_blocks; ++l) {
     const int rc = forward_impl(&bc, cur, cond, &w->blocks[l], positions, nxt, at<void>(ws, p.block),
                                 p.block_bytes, stream, nullptr, 0,
                                 mods ? mods + (size_t)l * 6 * D : nullptr, q ? &q[l] : nullptr,
-                                /*lean=*/q != nullptr);
+                                /*lean=*/q != nullptr, /*table_ready=*/true);
     if (rc != H3DIT_OK) return rc;
     float *t = cur;
     cur = nxt;
