@@ -73,6 +73,63 @@ def block_flops(cfg) -> float:
     return 2.0 * T * (3 * A * D + A * D + 2 * D * F) + 4.0 * T * T * A + 2.0 * 6 * D * D
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock and board power from sysfs
+    (pp_dpm_sclk: the level marked '*' is the present clock; hwmon power1_input
+    in microwatts) every few milliseconds on a host thread, while the GPU works
+    through already-queued forwards. Reports nothing where the files are absent."""
+
+    def __init__(self, period_s: float = 0.004):
+        import glob
+        import threading
+        self.period = period_s
+        dev = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.sclk = dev[0] if dev else None
+        pw = sorted(glob.glob(os.path.join(os.path.dirname(dev[0]), "hwmon", "*", "power1_input"))) if dev else []
+        self.power = pw[0] if pw else None
+        self.mhz, self.watts = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            with open(self.sclk) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        self.mhz.append(float(line.split(":")[1].strip().lower().split("mhz")[0]))
+            if self.power:
+                with open(self.power) as f:
+                    self.watts.append(float(f.read()) * 1e-6)
+        except (OSError, ValueError, IndexError):
+            pass
+
+    def _run(self):
+        while not self._stop.is_set():
+            self._read()
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.sclk:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self.sclk:
+            self._stop.set()
+            self._thread.join()
+
+    def summary(self):
+        if not self.mhz:
+            return None
+        m = sorted(self.mhz)
+        out = {"mean_mhz": round(sum(m) / len(m)), "median_mhz": round(m[len(m) // 2]),
+               "min_mhz": round(m[0]), "max_mhz": round(m[-1]), "samples": len(m),
+               "source": "pp_dpm_sclk, sampled during the timed forwards"}
+        if self.watts:
+            out["mean_board_power_w"] = round(sum(self.watts) / len(self.watts), 1)
+        return out
+
+
 def measure(cfg, steps: int, warmup: int, linears: str = "bf16"):
     import torch
     from joint_attention_dit_amd import binding as B
@@ -94,12 +151,13 @@ def measure(cfg, steps: int, warmup: int, linears: str = "bf16"):
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     assert all(e.cuda_event for row in ev for e in row)
-    # the headline: K plain forwards
-    start.record(stream)
-    for _ in range(steps):
-        blk.forward(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
+    # the headline: K plain forwards (the clock sampled meanwhile on the host)
+    with ClockSampler() as clock:
+        start.record(stream)
+        for _ in range(steps):
+            blk.forward(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     # per-kernel times: K forwards with the library's events between its launches
     start.record(stream)
@@ -116,7 +174,8 @@ def measure(cfg, steps: int, warmup: int, linears: str = "bf16"):
                                  0.5 * (per_step[steps // 2 - 1] + per_step[steps // 2]), 4),
               "min_ms": round(per_step[0], 4), "max_ms": round(per_step[-1], 4),
               "mean_ms_with_stage_events": round(ms_timed, 4),
-              "of": "single forwards of the pass with stage events"}
+              "of": "single forwards of the pass with stage events",
+              "sclk": clock.summary()}
     out_ok = bool(torch.isfinite(blk.out).all().item())
     del blk
     torch.cuda.empty_cache()
@@ -808,6 +867,7 @@ def main():
         return
     ms, stage_ms, ok, spread = measure(cfg, args.steps, args.warmup, args.linears)
     tflops, kernels, roof = summarize(cfg, ms, stage_ms, args.linears)
+    sclk = spread.pop("sclk")
 
     rec = {
         "metric": METRIC,
@@ -829,6 +889,12 @@ def main():
                    "ffn": cfg.ffn},
         "tflops": round(tflops, 1),
         "pct_bf16_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        # the shader clock the chip held during the timed forwards, and the same
+        # rate against the dense peak at that clock (the chip lowers its clock
+        # under sustained matrix-core load)
+        "sclk": sclk,
+        "pct_bf16_mfma_peak_at_sclk": (round(100 * tflops / (PEAK_BF16_TFLOPS * sclk["mean_mhz"] / 2400.0), 2)
+                                       if sclk else None),
         "image_tokens_per_s": round(cfg.image_tokens / (ms * 1e-3), 1),
         "output_finite": ok,
         "kernels": kernels,
@@ -840,7 +906,7 @@ def main():
                                 args.linears)
         etf, ekern, eroof = summarize(ecfg, ems, est, args.linears)
         rec["extra"] = {"workload": ecfg.description, "n_tokens": ecfg.n_tokens,
-                        "ms_per_step": round(ems, 4), "per_step": espread, "value": round(ecfg.n_tokens / (ems * 1e-3), 1),
+                        "ms_per_step": round(ems, 4), "per_step": espread, "sclk": espread.pop("sclk"), "value": round(ecfg.n_tokens / (ems * 1e-3), 1),
                         "unit": "block-tokens/s", "tflops": round(etf, 1),
                         "pct_bf16_mfma_peak": round(100 * etf / PEAK_BF16_TFLOPS, 2),
                         "kernels": ekern}
