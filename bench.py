@@ -79,11 +79,11 @@ class ClockSampler:
     in microwatts) every few milliseconds on a host thread, while the GPU works
     through already-queued forwards. Reports nothing where the files are absent."""
 
-    def __init__(self, period_s: float = 0.004):
+    def __init__(self, period_s: float = 0.004, root: str = "/sys/class/drm"):
         import glob
         import threading
         self.period = period_s
-        dev = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        dev = sorted(glob.glob(os.path.join(root, "card*", "device", "pp_dpm_sclk")))
         self.sclk = dev[0] if dev else None
         pw = sorted(glob.glob(os.path.join(os.path.dirname(dev[0]), "hwmon", "*", "power1_input"))) if dev else []
         self.power = pw[0] if pw else None

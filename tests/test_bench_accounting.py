@@ -115,3 +115,17 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_clock_sampler_reads_the_marked_level(tmp_path):
+    dev = tmp_path / "card0" / "device"
+    (dev / "hwmon" / "hwmon3").mkdir(parents=True)
+    (dev / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 1821Mhz *\n2: 2400Mhz\n")
+    (dev / "hwmon" / "hwmon3" / "power1_input").write_text("1161800000\n")
+    c = bench.ClockSampler(period_s=0.001, root=str(tmp_path))
+    c._read()
+    c._read()
+    out = c.summary()
+    assert out["mean_mhz"] == 1821 and out["min_mhz"] == 1821 and out["samples"] == 2
+    assert out["mean_board_power_w"] == pytest.approx(1161.8)
+    assert bench.ClockSampler(root=str(tmp_path / "none")).summary() is None
