@@ -1,6 +1,6 @@
 """Host-side checks of bench.py's accounting (no GPU): the FLOP and byte counts
-the roofline is priced with, the trace and counter parsers, the digest that
-ties stored counter figures to the kernel sources, and the one-GPU guard."""
+the roofline is priced with, the trace parser, the digest that ties stored
+counter figures to the kernel sources, the clock sampler and the one-GPU guard."""
 import csv
 import os
 import shutil
