@@ -167,6 +167,49 @@ __global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(
   }
 }
 
+// Rounds 8 fp64 values once to bf16 (nearest, ties to even) by way of fp32:
+// f = fp32(o) rounds to nearest, and rounding f to bf16 then gives o's own bf16
+// rounding unless f sits exactly on a midpoint between two bf16 values while o
+// does not (o lies just beside that midpoint and f landed on it). Only then is
+// f moved one fp32 step toward o, so that the bf16 rounding goes o's way. The
+// check is two integer operations per value and the fix a wave-uniform branch
+// that a wave's chunk of 8 x 64 values takes about once in a hundred times;
+// the compiler's exact fp64-to-bf16 conversion costs about eight operations
+// each. value(j) recomputes o[j] for the fix (from operands it reloads), so the
+// doubles need not stay in registers until then.
+template <typename F>
+__device__ __forceinline__ void round8_via_f32(float f[8], F value) {
+  uint64_t tie = 0;  // the lanes with a value on a midpoint (one compare and a scalar or each)
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    tie |= __builtin_amdgcn_ballot_w64((__builtin_bit_cast(uint32_t, f[j]) & 0xFFFFu) == 0x8000u);
+  if (__builtin_expect(tie != 0, 0)) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t u = __builtin_bit_cast(uint32_t, f[j]);
+      const double o = value(j);
+      if ((u & 0xFFFFu) == 0x8000u && (double)f[j] != o)
+        f[j] = __builtin_bit_cast(float, fabs((double)f[j]) < fabs(o) ? u + 1u : u - 1u);
+    }
+  }
+}
+
+// Store 8 values (already adjusted by round8_via_f32) as bf16, or fp32 ones.
+__device__ __forceinline__ void store8f(bf16 *p, const float f[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const bf16x2 t = pack2(f[j], f[j + 1]);
+    v[j] = t[0];
+    v[j + 1] = t[1];
+  }
+  *reinterpret_cast<bf16x8 *>(p) = v;
+}
+__device__ __forceinline__ void store8f(float *p, const float f[8]) {
+  *reinterpret_cast<f32x4 *>(p) = f32x4{f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4 *>(p + 4) = f32x4{f[4], f[5], f[6], f[7]};
+}
+
 // Persistent form for rows of up to 8192 elements: one workgroup per CU stages
 // (1 + scale) and shift (fp64) in LDS once, then each wave normalises rows
 // w, w + W, ... (W waves in all; w numbers the waves wave-major across the
@@ -175,6 +218,8 @@ __global__ __launch_bounds__(256) void rmsnorm_modulate_reg_kernel(
 // The per-row fp64 modulation vectors then come from LDS rather than from L2
 // (for bf16 rows they are 16x the row's own bytes), and the many waves per CU
 // (16 for bf16 rows, 12 for fp32 rows) keep enough row loads in flight.
+// The fp64 results are rounded by round8_via_f32 (fp32 output: the plain
+// rounding to fp32).
 // LDS layout: element 8 c + 2 q + e of array a (0: 1 + scale, 1: shift) at
 // double index ((a * 4 + q) * 64 NC + c) * 2 + e (NC: chunks per lane), so the
 // 16-byte reads of consecutive lanes (consecutive c) are consecutive and every
@@ -185,6 +230,7 @@ template <typename XT, int NC, bool MX>
 struct LdsNorm {
   static constexpr int waves = (sizeof(XT) == 2 ? 16 : 12) - (MX || NC > 11 ? 4 : 0);
   static constexpr int threads = 64 * waves;
+  static constexpr size_t lds_bytes = (size_t)2 * 8 * 64 * NC * sizeof(double);
 };
 
 // Keeps v opaque to the compiler between the two passes, so it re-converts
@@ -240,26 +286,32 @@ __global__ __launch_bounds__((LdsNorm<XT, NC, MX>::threads)) void rmsnorm_modula
     for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
       if (c < chunks) {
-        double sc1[8], sh[8];
+        // element j of chunk cc from the LDS vectors: (1 + scale) and shift
+        auto mod = [&](int cc, int arr, int j) {
+          return mod_lds[((arr * 4 + (j >> 1)) * PL + cc) * 2 + (j & 1)];
+        };
+        const typename Chunk8<XT>::raw vi = v[i];
+        float f[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f64x2 a = *reinterpret_cast<const f64x2 *>(mod_lds + ((0 * 4 + q) * PL + c) * 2);
-          const f64x2 b = *reinterpret_cast<const f64x2 *>(mod_lds + ((1 * 4 + q) * PL + c) * 2);
-          sc1[2 * q] = a[0];
-          sc1[2 * q + 1] = a[1];
-          sh[2 * q] = b[0];
-          sh[2 * q + 1] = b[1];
+        for (int j = 0; j < 8; ++j)
+          f[j] = (float)((double)Chunk8<XT>::at(vi, j) * rs * mod(c, 0, j) + mod(c, 1, j));
+        if constexpr (std::is_same<OT, bf16>::value) {
+          round8_via_f32(f, [&](int j) {
+            // opaque copies: the compiler reloads the operands instead of
+            // keeping the fast path's doubles alive for this rare branch
+            int cc = c;
+            double r = rs;
+            asm volatile("" : "+v"(cc), "+v"(r));
+            return (double)Chunk8<XT>::at(vi, j) * r * mod(cc, 0, j) + mod(cc, 1, j);
+          });
         }
-        double o[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = (double)Chunk8<XT>::at(v[i], j) * rs * sc1[j] + sh[j];
-        if (!MX || h) store8<OT>(h + (int64_t)row * D + c * 8, o);  // MX: h may be left out
+        if (!MX || h) store8f(h + (int64_t)row * D + c * 8, f);  // MX: h may be left out
         if constexpr (MX) {
           float g[8];
           uint32_t amax = 0;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const bf16 bv = to_bf16(o[j]);
+            const bf16 bv = to_bf16(f[j]);
             g[j] = (float)bv;
             amax = max(amax, (uint32_t)__builtin_bit_cast(uint16_t, bv) & 0x7FFFu);
           }
@@ -328,9 +380,9 @@ static hipError_t launch_rn_lds(const void *x, bool x_is_f32, const double *shif
                                 uint8_t *codes, uint8_t *scales) {
   auto go = [&](auto nc_c) {
     constexpr int NC = decltype(nc_c)::value;
-    const size_t lds = (size_t)16 * 64 * 8 * NC;  // 2 arrays x 4 planes x 64 NC x 16 bytes
     if (x_is_f32) {
       auto k = rmsnorm_modulate_lds_kernel<float, NC, OT, MX>;
+      constexpr size_t lds = LdsNorm<float, NC, MX>::lds_bytes;
       hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)lds);
       if (e != hipSuccess) return e;
@@ -339,6 +391,7 @@ static hipError_t launch_rn_lds(const void *x, bool x_is_f32, const double *shif
                          shift, scale, h, T, D, (double)eps, codes, scales);
     } else {
       auto k = rmsnorm_modulate_lds_kernel<bf16, NC, OT, MX>;
+      constexpr size_t lds = LdsNorm<bf16, NC, MX>::lds_bytes;
       hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          (int)lds);
       if (e != hipSuccess) return e;

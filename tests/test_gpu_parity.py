@@ -82,6 +82,38 @@ def test_stage_rmsnorm_modulate(cfg):
     assert ulp.max() <= 1 and np.mean(ulp > 0) < 1e-3, (ulp.max(), np.mean(ulp > 0))
 
 
+@pytest.mark.parametrize("cfg", [MID, MID32], ids=lambda c: c.name)
+def test_stage_rmsnorm_rounds_like_fp64_beside_bf16_midpoints(cfg):
+    """Shifts chosen so that, in each column, one element's fp64 value lies
+    2^-28 (relative) above or below a midpoint between two bf16 values: its
+    rounding to fp32 lands on the midpoint, and only the fp64 value says which
+    way the bf16 rounding goes. The kernel's output must be the oracle's, bit
+    for bit, on those elements and on every other one."""
+    inp = cached_case(cfg)
+    say(f"[stage] rmsnorm midpoints {cfg.name} T={cfg.n_tokens} D={cfg.hidden} x={cfg.x_dtype}")
+    x, cond, w, pos = oracle_inputs(inp)
+    T, D = x.shape
+    scale = O.split_modulation(O.modulation(w["w_ada"], cond), D)["scale1"]
+    rng = np.random.default_rng(7)
+    rows, cols = rng.integers(0, T, size=D), np.arange(D)
+    prod = O.rms_normalize(x, cfg.eps)[rows, cols] * (1.0 + scale)
+    # the midpoint above a bf16 value a (in magnitude): a's bits with bit 15 set
+    u = (rng.standard_normal(D) * np.maximum(np.abs(prod), 0.5)).astype(np.float32)
+    mid = ((u.view(np.uint32) & 0xFFFF0000) | 0x8000).view(np.float32).astype(np.float64)
+    side = rng.choice([-1.0, 1.0], size=D)
+    shift = mid * (1.0 + side * 2.0 ** -28) - prod
+    value = O.rms_normalize(x, cfg.eps)[rows, cols] * (1.0 + scale) + shift
+    assert np.mean(value.astype(np.float32) == mid) > 0.99  # fp32 lands on the midpoint
+    c = B.config_from(cfg)
+    h = torch.empty(T, D, dtype=torch.bfloat16, device="cuda")
+    B.h3dit_rmsnorm_modulate(c, dev(inp["x"]), f64_dev(shift), f64_dev(scale), h)
+    ref = O.modulated_norm(x, shift, scale, cfg.eps, "contract")
+    up = np.abs(ref[rows, cols]) > np.abs(mid)
+    assert 0.3 < np.mean(up) < 0.7, np.mean(up)  # both directions are exercised
+    ulp = bf16_ulp_diff(host(h), ref)
+    assert ulp[rows, cols].max() == 0 and ulp.max() == 0, (ulp[rows, cols].max(), ulp.max())
+
+
 @pytest.mark.parametrize("cfg", SMALL_CASES, ids=lambda c: c.name)
 def test_stage_rope_table(cfg):
     inp = cached_case(cfg)
